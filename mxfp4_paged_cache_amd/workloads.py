@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for paged MXFP4 index scoring.
+
+This module holds no arithmetic of the scoring method: it only draws random
+bytes and values and lays them out. Both the HIP path and the CPU oracle are
+fed from it, so it must stay free of decoding, rounding rules or scoring.
+
+Recipe (the pages' scorer benchmarks use random K data with e8m0 bytes in
+[122, 127] and Q drawn per row; aiter #7061, "Performance"):
+* Q: N(0, 1) fp32 draws cast by torch to bf16, or to float8_e4m3fn where a
+  workload hands the query over as e4m3;
+* K data: uniform random bytes, so both e2m1 codes of a byte are uniform over
+  all 16 codes;
+* K scales: uniform random e8m0 bytes in [lo, hi] per (token, 32-element block);
+* block table: distinct pages drawn without replacement from a larger pool, so
+  the gather is a real random gather;
+* cu_seqlens_q / seq_lens / prefix_lens: as the workload states.
+
+Streams: one torch.Generator per field, seeded with (seed, field id), so a
+field can be regenerated without the others.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+D = 128                    # head dim: 64 B of e2m1 data + 4 e8m0 bytes per token
+SLOT_DATA_BYTES = 64
+SLOT_SCALE_BYTES = 4
+
+F_Q, F_KDATA, F_KSCALE, F_TABLE, F_POISON = range(5)
+
+
+@dataclass
+class Workload:
+    name: str
+    mode: str                       # "prefill" | "decode" | "logits"
+    H: int
+    page_size: int
+    q_lens: List[int]               # per request (decode: all 1)
+    prefix_lens: List[int]
+    seq_lens: List[int]
+    q_dtype: str = "bf16"           # "bf16" | "e4m3"
+    scale_lo: int = 122
+    scale_hi: int = 127
+    pool_pages: int = 0             # 0 -> exactly the pages the requests need
+    want_logits: bool = False
+    want_blocks: bool = True
+    layout: str = "split"           # "split" | "region" | "shared"
+    shared_first_page: int = 0      # physical id of the first used page ("shared")
+    table_pad: int = 0              # extra -1 entries per block-table row
+    table_width: int = 0            # minimum block-table width
+    table_fill: str = "pad"         # entries past a request's pages: "pad" (-1) or "perm" (more distinct pages)
+    max_seq_len: Optional[int] = None
+    tables: int = 1                 # disjoint block tables (benchmark rotation)
+    note: str = ""
+
+    @property
+    def B(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def T(self) -> int:
+        return sum(self.q_lens)
+
+    @property
+    def window(self) -> int:
+        return self.max_seq_len if self.max_seq_len is not None else max(self.seq_lens, default=0)
+
+    @property
+    def NB(self) -> int:
+        return (self.window + self.page_size - 1) // self.page_size
+
+    def limits(self) -> List[int]:
+        """Live-token count per query row, in row order."""
+        out = []
+        for b in range(self.B):
+            for i in range(self.q_lens[b]):
+                if self.mode == "decode":
+                    lim = self.seq_lens[b]
+                else:
+                    lim = min(self.seq_lens[b], self.prefix_lens[b] + i + 1)
+                out.append(max(0, min(lim, self.window)))
+        return out
+
+    def live_triples(self) -> int:
+        return sum(self.limits()) * self.H
+
+    def pages_per_request(self) -> List[int]:
+        return [(s + self.page_size - 1) // self.page_size for s in self.seq_lens]
+
+
+def _gen(seed: int, fid: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + fid * 7919 + 17)
+    return g
+
+
+@dataclass
+class Inputs:
+    wl: Workload
+    q: torch.Tensor                 # [T, H, 128] bf16 or float8_e4m3fn (may be a strided view)
+    k_data: torch.Tensor            # uint8 view [pages, P, 64]
+    k_scale: torch.Tensor           # uint8 view [pages, P, 4]
+    block_tables: List[torch.Tensor]  # int32 [B, width], one per rotation
+    cu_seqlens_q: torch.Tensor      # int32 [B+1]
+    seq_lens: torch.Tensor          # int32 [B]
+    prefix_lens: torch.Tensor       # int32 [B]
+    region: Optional[torch.Tensor] = None   # backing uint8 region for "region"/"shared"
+    extras: dict = field(default_factory=dict)
+
+    @property
+    def block_table(self) -> torch.Tensor:
+        return self.block_tables[0]
+
+
+def make_q(wl: Workload, seed: int, device="cpu", q_strided: bool = False) -> torch.Tensor:
+    g = _gen(seed, F_Q, device)
+    T = wl.T
+    x = torch.randn((T, wl.H, D), generator=g, device=device, dtype=torch.float32)
+    dt = torch.bfloat16 if wl.q_dtype == "bf16" else torch.float8_e4m3fn
+    if not q_strided:
+        return x.to(dt)
+    # strided rows: every row padded by 64 extra elements, heads padded by 128
+    big = torch.zeros((T, wl.H, 2 * D), device=device, dtype=dt)
+    big[:, :, :D] = x.to(dt)
+    return big[:, :, :D]
+
+
+def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = False) -> Inputs:
+    P = wl.page_size
+    npr = wl.pages_per_request()
+    need = sum(npr)
+    width = max(max(npr, default=0), wl.NB, wl.table_width) + wl.table_pad
+    per_table = need if wl.table_fill == "pad" else wl.B * width
+    pool = max(wl.pool_pages, per_table * wl.tables)
+    if wl.layout == "shared":
+        pool = max(pool, wl.shared_first_page + need * wl.tables)
+
+    gd = _gen(seed, F_KDATA, device)
+    gs = _gen(seed, F_KSCALE, device)
+    gt = _gen(seed, F_TABLE, "cpu")
+
+    region = None
+    if wl.layout == "split":
+        k_data = torch.randint(0, 256, (pool, P, SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
+        k_scale = torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, P, SLOT_SCALE_BYTES), generator=gs,
+                                device=device, dtype=torch.uint8)
+    else:
+        # One uint8 region. "region": page = [P x 64 B data][P x 4 B scale].
+        # "shared": page block = two layer slots of that shape; slot 1 is scored,
+        # every byte outside the scored pages is 0xFF (e2m1 -6, e8m0 NaN).
+        slot = P * (SLOT_DATA_BYTES + SLOT_SCALE_BYTES)
+        stride = slot if wl.layout == "region" else 2 * slot
+        off = 0 if wl.layout == "region" else slot
+        region = torch.full((pool * stride,), 0xFF, device=device, dtype=torch.uint8)
+        view = region.view(pool, stride)
+        lo = wl.shared_first_page if wl.layout == "shared" else 0
+        hi = pool
+        nused = hi - lo
+        data_part = torch.randint(0, 256, (nused, P * SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
+        scale_part = torch.randint(wl.scale_lo, wl.scale_hi + 1, (nused, P * SLOT_SCALE_BYTES), generator=gs,
+                                   device=device, dtype=torch.uint8)
+        view[lo:hi, off:off + P * SLOT_DATA_BYTES] = data_part
+        view[lo:hi, off + P * SLOT_DATA_BYTES:off + slot] = scale_part
+        k_data = torch.as_strided(region, (pool, P, SLOT_DATA_BYTES), (stride, SLOT_DATA_BYTES, 1), off)
+        k_scale = torch.as_strided(region, (pool, P, SLOT_SCALE_BYTES), (stride, SLOT_SCALE_BYTES, 1),
+                                   off + P * SLOT_DATA_BYTES)
+
+    # block tables: distinct pages; rotations use disjoint page sets
+    lo = wl.shared_first_page if wl.layout == "shared" else 0
+    perm = torch.randperm(pool - lo, generator=gt)[: per_table * wl.tables] + lo
+    tables = []
+    for r in range(wl.tables):
+        bt = torch.full((wl.B, width), -1, dtype=torch.int32)
+        chunk = perm[r * per_table:(r + 1) * per_table]
+        pos = 0
+        for b in range(wl.B):
+            n = npr[b] if wl.table_fill == "pad" else width
+            bt[b, :n] = chunk[pos:pos + n].to(torch.int32)
+            pos += n
+        tables.append(bt.to(device))
+
+    cu = [0]
+    for ql in wl.q_lens:
+        cu.append(cu[-1] + ql)
+    return Inputs(
+        wl=wl,
+        q=make_q(wl, seed, device, q_strided),
+        k_data=k_data,
+        k_scale=k_scale,
+        block_tables=tables,
+        cu_seqlens_q=torch.tensor(cu, dtype=torch.int32, device=device),
+        seq_lens=torch.tensor(wl.seq_lens, dtype=torch.int32, device=device),
+        prefix_lens=torch.tensor(wl.prefix_lens, dtype=torch.int32, device=device),
+        region=region,
+    )
+
+
+# ---------------------------------------------------------------- workloads
+
+INV_SQRT_D = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))   # RN32(1/sqrt(128))
+
+
+def prefill_small() -> Workload:
+    """64 query rows after a 960-token prefix, context 1024, 16-page pool, logits + block scores."""
+    return Workload("prefill_q64_ctx1k", "prefill", H=64, page_size=128, q_lens=[64], prefix_lens=[960],
+                    seq_lens=[1024], pool_pages=16, want_logits=True, table_width=16, table_fill="perm")
+
+
+def decode_b64_128k(tables: int = 1) -> Workload:
+    """B=64 decode rows, context 131072 (1024 pages each), pages drawn from a 300k-page pool."""
+    return Workload("decode_b64_ctx128k", "decode", H=64, page_size=128, q_lens=[1] * 64,
+                    prefix_lens=[131071] * 64, seq_lens=[131072] * 64, pool_pages=300_000, tables=tables)
+
+
+def prefill_long() -> Workload:
+    """4096 query rows after a 126976-token prefix (context 131072), e4m3 Q given directly."""
+    return Workload("prefill_q4096_ctx128k", "prefill", H=64, page_size=128, q_lens=[4096], prefix_lens=[126976],
+                    seq_lens=[131072], q_dtype="e4m3", pool_pages=300_000)
+
+
+def prefill_chunk() -> Workload:
+    """32768-row chunk after a 100000-token prefix (context 132768), e8m0 bytes uniform in 100..150."""
+    return Workload("prefill_chunk32k_ctx132768", "prefill", H=64, page_size=128, q_lens=[32768],
+                    prefix_lens=[100000], seq_lens=[132768], scale_lo=100, scale_hi=150, pool_pages=300_000)
+
+
+def logits_shared_pool() -> Workload:
+    """Logits mode, 64-token pages in a shared two-slot region past byte offset 4.608e9, B=8 x 128 rows, ctx 8192."""
+    return Workload("logits_b8_q128_ctx8k_shared", "logits", H=64, page_size=64, q_lens=[128] * 8,
+                    prefix_lens=[8064] * 8, seq_lens=[8192] * 8, want_logits=True, want_blocks=False,
+                    layout="shared", shared_first_page=529_412, table_pad=8)
+
+
+CONFIGS = {
+    1: prefill_small,
+    2: decode_b64_128k,
+    3: prefill_long,
+    4: prefill_chunk,
+    5: logits_shared_pool,
+}
