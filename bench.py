@@ -1,0 +1,235 @@
+"""Benchmark of the paged MXFP4 index scorer on one MI355X.
+
+Default workload: decode, B = 64 requests, one query row each, context
+131072 (1024 pages of 128 tokens per request), H = 64, D = 128, bf16 query
+~ N(0, 1), e2m1 codes uniform, e8m0 bytes uniform in [122, 127], pages drawn
+without replacement from a 300k-page pool (2.6 GB). A step is one scorer
+call over the whole batch; four disjoint block tables rotate between steps
+so consecutive calls read different pages (the pool defeats the 256 MB
+last-level cache). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (stdout). Throughput is live scored (row x head x token)
+triples per second; the line also carries us/call, achieved HBM GB/s and
+scaled-MFMA utilisation, the roofline of the dominant kernel and the CPU
+oracle's rate on a bounded sample of the same workload.
+
+--config selects another workload (1: prefill 64 rows ctx 1k with logits,
+3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
+5: logits, 64-token pages in a shared pool past 4.608e9 bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+MFMA_FP8_PEAK_TFLOPS = 5000.0     # dense fp8 rate; the fp4 x fp8 scaled MFMA issues at this rate
+MFMA_FP4_PEAK_TFLOPS = 10100.0    # dense fp4 x fp4, for reference
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, inp) -> int:
+    """Bytes a call must move at minimum: every live page once (data + scales),
+    the query rows, the block-table entries of live pages, and every output
+    element written once."""
+    P = wl.page_size
+    pages = sum((min(s, wl.window) + P - 1) // P for s in wl.seq_lens)
+    kbytes = pages * P * 68
+    qbytes = wl.T * wl.H * 128 * (2 if wl.q_dtype == "bf16" else 1)
+    table = pages * 4
+    out = 0
+    if wl.want_blocks:
+        out += wl.T * wl.H * wl.NB * 4
+    if wl.want_logits:
+        out += wl.T * wl.H * wl.window * 4
+    meta = (wl.B * 3 + 1) * 4
+    return kbytes + qbytes + table + out + meta
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="rows the oracle scores for the CPU baseline")
+    ap.add_argument("--traffic", type=str, default="", help="JSON file with measured HBM bytes per launch")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the scorer needs no "
+              f"collective; see DESIGN.md for how the path shards)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_paged_cache_amd as mx
+    from mxfp4_paged_cache_amd import workloads as W
+
+    if not os.path.exists(mx.library_path()):
+        from mxfp4_paged_cache_amd import build as mxbuild
+        mxbuild.build(force=True)
+    mx.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = W.CONFIGS[args.config]()
+    if wl.mode == "decode":
+        wl.tables = 4
+    log(f"workload {wl.name}: generating inputs on the GPU")
+    t0 = time.time()
+    inp = W.make_inputs(wl, args.seed, dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    T, H, P = wl.T, wl.H, wl.page_size
+    NB, Wd = wl.NB, wl.window
+    S = W.INV_SQRT_D
+
+    bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if wl.want_blocks else None
+    lg = torch.empty((T, H, Wd), dtype=torch.float32, device=dev) if wl.want_logits else None
+    plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks)
+    log(f"plan: {plan.as_dict()}")
+
+    def call(i):
+        bt = inp.block_tables[i % len(inp.block_tables)]
+        if wl.mode == "decode":
+            mx.score_decode(inp.q, inp.k_data, inp.k_scale, bt, inp.seq_lens, Wd, S, out=bs,
+                            logits=lg if lg is not None else False, plan=plan)
+        elif wl.mode == "logits":
+            mx.score_logits(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                            max(wl.q_lens), Wd, S, out=lg, block_scores=bs if bs is not None else False, plan=plan)
+        else:
+            mx.score_prefill(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                             max(wl.q_lens), Wd, S, out=bs, logits=lg if lg is not None else False, plan=plan)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms = ms_total / args.steps   # one kernel launch per step: this is the launch's average duration
+
+    triples = wl.live_triples()
+    value = triples / (ms / 1e3)
+    abytes = algorithmic_bytes(wl, inp)
+    flops = 2.0 * 128 * triples
+    gbps = abytes / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64)
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == wl.name:
+            traffic = tr.get("bytes_per_launch")
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_sample)
+
+    line = {
+        "metric": "scored (row x head x token) triples/s; us/call, HBM GB/s and scaled-MFMA util alongside",
+        "value": value,
+        "unit": "(row x head x token)/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_call": ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1 x e4m3 -> f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "query_rows": T, "heads": H, "head_dim": 128,
+                   "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype,
+                   "e8m0_range": [wl.scale_lo, wl.scale_hi], "outputs": ("block_scores" if wl.want_blocks else "") +
+                   ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables)},
+        "hbm_gbps": round(gbps, 1),
+        "mfma_tflops": round(tflops, 2),
+        "mfma_util_fp8_rate": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+        "algorithmic_bytes": abytes,
+        "live_triples": triples,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, inp, sample_rows: int):
+    """The oracle (test infrastructure, untuned) on a bounded sample of the same
+    workload, timed on this host's cores; reported as triples/s."""
+    import numpy as np
+    import torch
+    import oracle
+
+    oracle.build()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+    T = wl.T
+    if sample_rows <= 0:
+        sample_rows = {"decode": 16}.get(wl.mode, 4)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(T, size=min(sample_rows, T), replace=False)).astype(np.int32)
+    lim = wl.limits()
+    sample_triples = int(sum(lim[r] for r in rows)) * wl.H
+    # host copies of exactly the pages the sampled requests use (page order is irrelevant)
+    mode = "decode" if wl.mode == "decode" else "prefill"
+    bt = inp.block_tables[0].cpu().numpy()
+    cu = inp.cu_seqlens_q.cpu().numpy()
+    reqs = rows if mode == "decode" else np.unique(np.searchsorted(cu, rows, side="right") - 1)
+    keep = np.zeros(bt.shape[0], bool)
+    keep[reqs] = True
+    bt = np.where(keep[:, None], bt, -1)
+    used = np.unique(bt[bt >= 0])
+    idx = torch.as_tensor(used, dtype=torch.long, device=inp.k_data.device)
+    kd = inp.k_data.index_select(0, idx).cpu().numpy()
+    ks = inp.k_scale.index_select(0, idx).cpu().numpy()
+    remap = np.full(int(bt.max()) + 1, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    bt = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    qc = inp.q.cpu()
+    q = qc.view(torch.int16).numpy().view(np.uint16) if qc.dtype == torch.bfloat16 else qc.view(torch.uint8).numpy()
+    t0 = time.perf_counter()
+    oracle.score(mode=mode, q=q, q_dtype=wl.q_dtype, k_data=kd, k_scale=ks, page_size=wl.page_size, block_table=bt,
+                 seq_lens=inp.seq_lens.cpu().numpy(), max_seq_len=wl.window, sm_scale=float(np.float32(1 / np.sqrt(128))),
+                 cu_seqlens_q=cu, prefix_lens=inp.prefix_lens.cpu().numpy(), rows=rows,
+                 want_logits=wl.want_logits, want_blocks=wl.want_blocks, num_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": sample_triples / dt, "unit": "(row x head x token)/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {T} query rows ({sample_triples} live triples, all heads and pages of "
+                      f"those rows), {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * mxscore.h -- C ABI of the MI355X (gfx950) paged MXFP4 index scorer.
+ *
+ * The library scores query rows against a paged MXFP4 index-K cache and
+ * writes fp32 logits scaled by sm_scale per (row, head, token) and per-page
+ * maxima ("block scores") per (row, head, page).
+ *
+ * Cache format (aiter #7061, "Format"): each token holds 128 elements as
+ * e2m1 codes, two per byte with element 2m in the low nibble of byte m
+ * (64 B), plus four e8m0 scale bytes, byte k scaling elements 32k..32k+31
+ * (4 B). Element value = e2m1(code) * 2^(byte - 127). A page holds P = 64 or
+ * 128 tokens. The caller picks the layout through two views, each with its
+ * own byte page stride (aiter #7061, "Format"; aiter #5518, "Summary"):
+ *     data  byte i of token j of page p: data  + p*data_page_stride  + j*64 + i
+ *     scale byte k of token j of page p: scale + p*scale_page_stride + j*4  + k
+ * Split tensors, a single-region page [P x 64 B data][P x 4 B scales] and a
+ * shared multi-slot pool past 4 GiB are all expressed this way; page offsets
+ * are computed in 64 bits.
+ *
+ * Query (aiter #7061, "Kernels"; ATOM #2770, write-path commit): 128
+ * elements per (row, head), bf16 rounded in-kernel to e4m3 (nearest even,
+ * saturating at +-448, unit scale), or e4m3 (OCP float8_e4m3fn) used as stored.
+ *
+ * Scores: logit(r, h, t) = RN_fp32(RN_fp32(dot) * sm_scale) for live tokens,
+ * where dot is the scaled-MFMA dot of Q_hat and K (see the error note below);
+ * -inf for dead tokens. block(r, h, j) = max over live tokens t of page j of
+ * logit(r, h, t), -inf when the page has none (aiter #7061, "Format").
+ * Live tokens of a prefill row i of request b: t < min(seq_len[b],
+ * prefix_len[b] + i + 1, max_seq_len); of a decode row b: t < min(seq_len[b],
+ * max_seq_len) (aiter #7061, "Kernels" and "Changed op tests").
+ *
+ * Arithmetic note: the dot uses gfx950's block-scaled fp4 x fp8 MFMA
+ * (ATOM #2770, squashed pa_decode MXFP4 commit: one
+ * v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens x 16 queries, the K e8m0
+ * byte as its block scale). Measured on gfx950: the instruction sums products
+ * across groups of 8 adjacent elements exactly and rounds once, but within a
+ * group keeps about 12 bits below the group's largest product. Results equal
+ * RN_fp32 of the exact dot except under cancellation, with
+ * |error| <= 2^-11 * sum_e |Q_hat[e] K[e]| in the worst measured case.
+ *
+ * Outputs: every element of the window is written: logits [rows, heads,
+ * max_seq_len] and block scores [rows, heads, ceil(max_seq_len / P)]; live
+ * entries get scores, everything else -inf, so no pre-fill is needed
+ * (aiter #5518, "Correctness": outputs poisoned between graph replays must
+ * be fully rewritten). Rows of requests with no query rows do not exist.
+ *
+ * Ownership and execution: every pointer in these structs is a device
+ * pointer owned by the caller. Calls validate all host-visible arguments
+ * first and touch no memory when they fail. A successful call enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the null stream), returns
+ * without synchronizing, allocates no device memory, keeps no pointer, and
+ * may be captured in a HIP graph. Device-side contract (not checked):
+ * cu_seqlens_q non-decreasing with cu_seqlens_q[B] == total_rows, each
+ * request's q_len <= max_query_len, block-table entries of live pages in
+ * [0, num_pages), e8m0 bytes of live tokens in [1, 254]. Entries past a
+ * request's live pages are never read (they may hold -1).
+ *
+ * Thread safety: calls may be made from several host threads; error text is
+ * kept per thread.
+ */
+#ifndef MXSCORE_H
+#define MXSCORE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define MXS_OK 0
+#define MXS_EINVAL (-1)       /* null pointer, negative count, sm_scale not finite and > 0 */
+#define MXS_EDTYPE (-2)       /* query dtype is neither bf16 nor e4m3 (fp16 is refused) */
+#define MXS_ELAYOUT (-3)      /* stride, alignment, page size or table width rule broken */
+#define MXS_EUNSUPPORTED (-4) /* current device is not gfx950, or no device */
+#define MXS_EDEVICE (-5)      /* HIP runtime error while launching */
+
+/* ---------------------------------------------------------------- dtypes / modes */
+#define MXS_Q_BF16 1
+#define MXS_Q_E4M3 2
+
+#define MXS_MODE_PREFILL 1
+#define MXS_MODE_DECODE 2
+#define MXS_MODE_LOGITS 3
+
+/* Paged MXFP4 cache views (see the layout above).
+ * data: 16-byte aligned, data_page_stride a multiple of 16 and >= 64 * page_size.
+ * scale: 4-byte aligned, scale_page_stride a multiple of 4 and >= 4 * page_size. */
+typedef struct mxs_kcache {
+  const void* data;
+  int64_t data_page_stride;    /* bytes */
+  const void* scale;
+  int64_t scale_page_stride;   /* bytes */
+  int32_t page_size;           /* 64 or 128 */
+  int64_t num_pages;           /* pages addressable through both views, >= 1 */
+} mxs_kcache;
+
+/* Query rows: element e of head h of row r at
+ * ptr + (r * row_stride + h * head_stride + e) * elem_size; head_dim 128 contiguous.
+ * ptr 16-byte aligned; row_stride and head_stride (elements, >= 0) times the
+ * element size multiples of 16 bytes. Prefill/logits rows are the
+ * concatenated query rows [total_rows]; decode rows are requests [batch]. */
+typedef struct mxs_query {
+  const void* ptr;
+  int32_t dtype;               /* MXS_Q_BF16 or MXS_Q_E4M3 */
+  int64_t row_stride;          /* elements */
+  int64_t head_stride;         /* elements */
+  int32_t num_heads;           /* >= 1 */
+} mxs_query;
+
+/* fp32 output [rows, heads, width], last axis contiguous:
+ * element (r, h, x) at ptr + r * row_stride + h * head_stride + x (elements).
+ * ptr 4-byte aligned; strides >= 0. A NULL ptr means "not requested". */
+typedef struct mxs_out {
+  float* ptr;
+  int64_t row_stride;
+  int64_t head_stride;
+} mxs_out;
+
+/* Request metadata (aiter #7061, "Kernels": block_table, cu_seqlens_q,
+ * seq_lens, prefix_lens, max_query_len, max_seq_len). Device int32 arrays,
+ * contiguous. bt_row_stride in int32 elements (aiter #5518, "Summary"). */
+typedef struct mxs_batch {
+  const int32_t* block_table;  /* [batch, bt_row_stride] */
+  int64_t bt_row_stride;       /* >= bt_width */
+  int32_t bt_width;            /* >= ceil(max_seq_len / page_size) */
+  const int32_t* cu_seqlens_q; /* [batch + 1]; prefill/logits only (ignored by decode) */
+  const int32_t* seq_lens;     /* [batch] */
+  const int32_t* prefix_lens;  /* [batch]; prefill/logits only (ignored by decode) */
+  int32_t batch;               /* >= 0 */
+  int32_t total_rows;          /* prefill/logits: cu_seqlens_q[batch]; decode: ignored */
+  int32_t max_query_len;       /* prefill/logits: >= every request's q_len; decode: ignored */
+  int32_t max_seq_len;         /* output window in tokens, >= 0 */
+} mxs_batch;
+
+/* Launch plan: a pure function of host integers (mode, shapes, page size,
+ * the device's CU count and the kernels' occupancy), so a captured graph
+ * replays the same launch (aiter #5518, decode auto-CTA: host-known buckets,
+ * no device-to-host sync). Plain old data; may be computed once and reused
+ * for every call with the same shapes. */
+typedef struct mxs_plan {
+  int32_t mode;
+  int32_t q_dtype;
+  int32_t page_size;
+  int32_t num_heads;
+  int32_t batch;
+  int32_t max_query_len;
+  int32_t max_seq_len;
+  int32_t want_logits;
+  int32_t want_blocks;
+  int32_t grid;                /* workgroups launched */
+  int32_t block;               /* threads per workgroup */
+  int32_t slots_per_item;      /* (row, head) query slots per work item */
+  int32_t pages_per_item;      /* pages per work item */
+  int32_t slot_items;          /* work items along the slot axis, per request */
+  int32_t page_items;          /* work items along the page axis, per request */
+  int32_t head_groups;         /* decode: groups of 64 heads */
+  int64_t items;               /* total work items */
+  int32_t kernel;              /* internal kernel id */
+  int32_t reserved;
+} mxs_plan;
+
+/* Compute a plan. parallel_unit_num > 0 overrides the workgroup count
+ * (aiter #5518: explicit parallel_unit_num remains an override); 0 = auto.
+ * For MXS_MODE_DECODE, max_query_len is ignored (1). Returns MXS_OK or an
+ * error code; writes *plan only on success. */
+int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+                  int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
+                  int32_t parallel_unit_num, mxs_plan* plan);
+
+/* The same planner as a pure function of its arguments: num_cus is the
+ * device's compute-unit count and wg_per_cu the workgroups of the chosen
+ * kernel resident per CU (mxs_plan_make reads both from the current device).
+ * Identical arguments always give an identical plan. */
+int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+                      int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
+                      int32_t parallel_unit_num, int32_t num_cus, int32_t wg_per_cu, mxs_plan* plan);
+
+/* Prefill block scorer (aiter #7061, "Kernels": score_prefill; the MXFP4
+ * index-cache prefill scorer). Rows are the request-concatenated query rows.
+ * block_scores required ([total_rows, H, NB]); logits optional
+ * ([total_rows, H, max_seq_len]). plan may be NULL (computed per call). */
+int mxs_score_prefill(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                      const mxs_out* block_scores, const mxs_out* logits, const mxs_plan* plan, void* stream);
+
+/* Decode block scorer (ATOM #2770, "How it works": the MXFP4 index decode
+ * scorer over the two views). One query row per request: q rows are the
+ * requests, limit = seq_len. block_scores required ([batch, H, NB]); logits
+ * optional ([batch, H, max_seq_len]). */
+int mxs_score_decode(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                     const mxs_out* block_scores, const mxs_out* logits, const mxs_plan* plan, void* stream);
+
+/* Logits-first scorer (aiter #5518, "Summary": paged MXFP4 MQA logits with
+ * ragged query lengths). Same arguments and masking as prefill, tiled for
+ * coalesced logit writes; logits required, block_scores optional. */
+int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                     const mxs_out* logits, const mxs_out* block_scores, const mxs_plan* plan, void* stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* mxs_last_error(void);
+
+/* Library version string. */
+const char* mxs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXSCORE_H */

@@ -1,0 +1,374 @@
+// Host side of the C ABI declared in include/mxscore.h: argument validation,
+// launch planning and dispatch. Everything here runs before any device work;
+// a rejected call touches no memory (aiter #7061, "Changed op tests":
+// rejections are raised before launch).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "mxs_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// a * b + c without overflow; returns false on overflow or negative inputs
+bool mul_add(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  if (a < 0 || b < 0 || c < 0) return false;
+  __int128 r = (__int128)a * b + c;
+  if (r > INT64_MAX) return false;
+  *out = (int64_t)r;
+  return true;
+}
+
+struct DeviceInfo {
+  int status = MXS_OK;
+  std::string why;
+  int cus = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_devices;
+std::map<uint64_t, int> g_occupancy;
+
+int current_device(int* dev, DeviceInfo* info) {
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0) {
+    (void)hipGetLastError();
+    return fail(MXS_EUNSUPPORTED, "no HIP device is available");
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_devices.find(d);
+  if (it == g_devices.end()) {
+    DeviceInfo di;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) {
+      (void)hipGetLastError();
+      di.status = MXS_EUNSUPPORTED;
+      di.why = "cannot query the current HIP device";
+    } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      di.status = MXS_EUNSUPPORTED;
+      di.why = std::string("the scorer needs gfx950 (MI355X); current device is ") + prop.gcnArchName;
+    } else {
+      di.cus = prop.multiProcessorCount;
+    }
+    it = g_devices.emplace(d, di).first;
+  }
+  *dev = d;
+  *info = it->second;
+  if (info->status != MXS_OK) return fail(info->status, "%s", info->why.c_str());
+  return MXS_OK;
+}
+
+int occupancy_cached(int dev, int32_t kernel, int32_t q_dtype, int32_t page_size) {
+  const uint64_t key = ((uint64_t)(uint32_t)dev << 32) | ((uint64_t)kernel << 16) | ((uint64_t)q_dtype << 8) |
+                       (uint64_t)(page_size == 128 ? 1 : 0);
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_occupancy.find(key);
+    if (it != g_occupancy.end()) return it->second;
+  }
+  const int occ = mxs::occupancy(kernel, q_dtype, page_size);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_occupancy[key] = occ;
+  return occ;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxs_last_error(void) { return g_error.c_str(); }
+
+const char* mxs_version(void) { return "mxscore 0.1 (gfx950)"; }
+
+// Pure planner: every input is a host integer; the same inputs give the same
+// plan. num_cus and wg_per_cu describe the device (CUs and resident
+// workgroups of the chosen kernel per CU).
+int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+                      int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
+                      int32_t parallel_unit_num, int32_t num_cus, int32_t wg_per_cu, mxs_plan* plan) {
+  if (!plan) return fail(MXS_EINVAL, "plan pointer is NULL");
+  if (mode != MXS_MODE_PREFILL && mode != MXS_MODE_DECODE && mode != MXS_MODE_LOGITS)
+    return fail(MXS_EINVAL, "unknown mode %d", mode);
+  if (q_dtype != MXS_Q_BF16 && q_dtype != MXS_Q_E4M3)
+    return fail(MXS_EDTYPE, "query dtype must be bf16 (%d) or e4m3 (%d); got %d (fp16 is refused)", MXS_Q_BF16,
+                MXS_Q_E4M3, q_dtype);
+  if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
+  if (num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", num_heads);
+  if (batch < 0 || max_seq_len < 0 || (mode != MXS_MODE_DECODE && max_query_len < 0))
+    return fail(MXS_EINVAL, "negative batch (%d), max_query_len (%d) or max_seq_len (%d)", batch, max_query_len,
+                max_seq_len);
+  if (parallel_unit_num < 0) return fail(MXS_EINVAL, "parallel_unit_num must be >= 0");
+  if (num_cus < 1 || wg_per_cu < 1) return fail(MXS_EINVAL, "device description must be positive");
+  if (mode == MXS_MODE_LOGITS && !want_logits) return fail(MXS_EINVAL, "logits mode needs logits");
+  if (mode != MXS_MODE_LOGITS && !want_blocks) return fail(MXS_EINVAL, "prefill and decode need block scores");
+
+  mxs_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.mode = mode;
+  p.q_dtype = q_dtype;
+  p.page_size = page_size;
+  p.num_heads = num_heads;
+  p.batch = batch;
+  p.max_query_len = mode == MXS_MODE_DECODE ? 1 : max_query_len;
+  p.max_seq_len = max_seq_len;
+  p.want_logits = want_logits ? 1 : 0;
+  p.want_blocks = want_blocks ? 1 : 0;
+  p.block = mxs::kThreads;
+  const int64_t NB = ceil_div(max_seq_len, page_size);
+  const int64_t capacity = (int64_t)num_cus * wg_per_cu;   // resident workgroups
+
+  if (mode == MXS_MODE_DECODE) {
+    // One wave per (request, 64-head group, page chunk). Chunks are sized so
+    // that the waves fill the resident capacity about once (aiter #5518,
+    // decode auto-CTA: host-known buckets), or the requested unit count.
+    p.kernel = mxs::KID_DECODE;
+    p.head_groups = (int32_t)ceil_div(num_heads, mxs::kDecodeHeads);
+    const int64_t lanes = (int64_t)batch * p.head_groups;
+    int64_t target_waves = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * mxs::kWaves : capacity * mxs::kWaves;
+    int64_t chunks = lanes > 0 ? ceil_div(target_waves, lanes) : 1;
+    if (chunks > NB) chunks = NB;
+    if (chunks < 1) chunks = 1;
+    p.pages_per_item = (int32_t)(NB > 0 ? ceil_div(NB, chunks) : 1);
+    p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, p.pages_per_item) : 1);
+    p.slot_items = 1;
+    p.slots_per_item = num_heads;
+    p.items = lanes * p.page_items;
+    p.grid = (int32_t)ceil_div(p.items, mxs::kWaves);
+  } else {
+    // Work item = (request, block of query slots, chunk of pages). Enough
+    // items for a few per resident workgroup; the grid loops over them.
+    p.kernel = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+    p.head_groups = 1;
+    p.slots_per_item = mxs::kWaves * mxs::kPrefillTiles * 16;
+    const int64_t slots = (int64_t)p.max_query_len * num_heads;
+    p.slot_items = (int32_t)(slots > 0 ? ceil_div(slots, p.slots_per_item) : 0);
+    const int64_t base = (int64_t)batch * p.slot_items;
+    const int64_t want_items = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * 4 : capacity * 4;
+    int64_t chunks = base > 0 ? ceil_div(want_items, base) : 1;
+    if (chunks > NB) chunks = NB;
+    if (chunks < 1) chunks = 1;
+    int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
+    p.pages_per_item = (int32_t)ppi;
+    p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, ppi) : 1);
+    p.items = base * p.page_items;
+    int64_t grid = parallel_unit_num > 0 ? parallel_unit_num : capacity;
+    if (grid > p.items) grid = p.items;
+    if (grid < 1) grid = 1;
+    p.grid = (int32_t)grid;
+  }
+  if (p.items > INT32_MAX * (int64_t)mxs::kWaves || p.grid > INT32_MAX) return fail(MXS_EINVAL, "problem too large");
+  *plan = p;
+  return MXS_OK;
+}
+
+int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+                  int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
+                  int32_t parallel_unit_num, mxs_plan* plan) {
+  int dev;
+  DeviceInfo info;
+  int rc = current_device(&dev, &info);
+  if (rc != MXS_OK) return rc;
+  if (q_dtype != MXS_Q_BF16 && q_dtype != MXS_Q_E4M3)
+    return fail(MXS_EDTYPE, "query dtype must be bf16 or e4m3; got %d", q_dtype);
+  if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
+  const int32_t kid = mode == MXS_MODE_DECODE ? mxs::KID_DECODE : mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+  const int occ = occupancy_cached(dev, kid, q_dtype, page_size);
+  return mxs_plan_make_for(mode, q_dtype, page_size, num_heads, batch, max_query_len, max_seq_len, want_logits,
+                           want_blocks, parallel_unit_num, info.cus, occ, plan);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_out(const char* name, const mxs_out* o, int64_t rows, int32_t H, int64_t width) {
+  if (!o || !o->ptr) return fail(MXS_EINVAL, "%s output pointer is NULL", name);
+  if (!aligned(o->ptr, 4)) return fail(MXS_ELAYOUT, "%s output is not 4-byte aligned", name);
+  if (o->row_stride < 0 || o->head_stride < 0) return fail(MXS_ELAYOUT, "%s output strides must be >= 0", name);
+  if (H > 1 && o->head_stride < width)
+    return fail(MXS_ELAYOUT, "%s output head stride %lld is narrower than its width %lld", name,
+                (long long)o->head_stride, (long long)width);
+  int64_t row_span;
+  if (!mul_add(H - 1, o->head_stride, width, &row_span)) return fail(MXS_ELAYOUT, "%s output span overflows", name);
+  if (rows > 1 && o->row_stride < row_span)
+    return fail(MXS_ELAYOUT, "%s output row stride %lld is narrower than one row (%lld)", name,
+                (long long)o->row_stride, (long long)row_span);
+  int64_t span;
+  if (!mul_add(rows - 1, o->row_stride, row_span, &span) || span > INT64_MAX / 4)
+    return fail(MXS_ELAYOUT, "%s output span overflows", name);
+  return MXS_OK;
+}
+
+int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt, float sm_scale,
+          const mxs_out* bs, const mxs_out* lg, const mxs_plan* plan_in, void* stream) {
+  if (!q || !k || !bt) return fail(MXS_EINVAL, "query, cache and batch descriptors must not be NULL");
+  if (q->dtype != MXS_Q_BF16 && q->dtype != MXS_Q_E4M3)
+    return fail(MXS_EDTYPE, "query dtype must be bf16 (%d) or e4m3 (%d); got %d (fp16 is refused)", MXS_Q_BF16,
+                MXS_Q_E4M3, q->dtype);
+  if (q->num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", q->num_heads);
+  if (k->page_size != 64 && k->page_size != 128)
+    return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", k->page_size);
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return fail(MXS_EINVAL, "sm_scale must be finite and > 0");
+  if (bt->batch < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  const bool decode = mode == MXS_MODE_DECODE;
+  if (!decode && (bt->total_rows < 0 || bt->max_query_len < 0))
+    return fail(MXS_EINVAL, "total_rows and max_query_len must be >= 0");
+  const bool want_bs = bs && bs->ptr;
+  const bool want_lg = lg && lg->ptr;
+  if (mode != MXS_MODE_LOGITS && !want_bs) return fail(MXS_EINVAL, "block_scores output is required");
+  if (mode == MXS_MODE_LOGITS && !want_lg) return fail(MXS_EINVAL, "logits output is required in logits mode");
+
+  const int32_t H = q->num_heads, P = k->page_size;
+  const int64_t rows = decode ? bt->batch : bt->total_rows;
+  const int64_t NB = ceil_div(bt->max_seq_len, P);
+  if (rows == 0 || bt->max_seq_len == 0 || bt->batch == 0) {
+    // nothing to write; still refuse descriptors that are wrong regardless of size
+    return MXS_OK;
+  }
+  // query
+  const int64_t es = q->dtype == MXS_Q_BF16 ? 2 : 1;
+  if (!q->ptr) return fail(MXS_EINVAL, "query pointer is NULL");
+  if (!aligned(q->ptr, 16)) return fail(MXS_ELAYOUT, "query rows must be 16-byte aligned");
+  if (q->row_stride < 0 || q->head_stride < 0) return fail(MXS_ELAYOUT, "query strides must be >= 0");
+  if ((q->row_stride * es) % 16 || (q->head_stride * es) % 16)
+    return fail(MXS_ELAYOUT, "query row and head strides must be multiples of 16 bytes (misaligned query rows)");
+  // cache
+  if (!k->data || !k->scale) return fail(MXS_EINVAL, "cache data and scale pointers must not be NULL");
+  if (!aligned(k->data, 16)) return fail(MXS_ELAYOUT, "cache data view must be 16-byte aligned");
+  if (!aligned(k->scale, 4)) return fail(MXS_ELAYOUT, "cache scale view must be 4-byte aligned");
+  if (k->data_page_stride < (int64_t)P * 64 || k->data_page_stride % 16)
+    return fail(MXS_ELAYOUT, "data page stride %lld must be a multiple of 16 and >= %d (narrow data view)",
+                (long long)k->data_page_stride, P * 64);
+  if (k->scale_page_stride < (int64_t)P * 4 || k->scale_page_stride % 4)
+    return fail(MXS_ELAYOUT, "scale page stride %lld must be a multiple of 4 and >= %d (narrow scale view)",
+                (long long)k->scale_page_stride, P * 4);
+  if (k->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
+  int64_t tmp;
+  if (!mul_add(k->num_pages, k->data_page_stride, 0, &tmp) || !mul_add(k->num_pages, k->scale_page_stride, 0, &tmp))
+    return fail(MXS_ELAYOUT, "cache span overflows 64 bits");
+  // batch metadata
+  if (!bt->block_table || !bt->seq_lens) return fail(MXS_EINVAL, "block_table and seq_lens must not be NULL");
+  if (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens))
+    return fail(MXS_EINVAL, "cu_seqlens_q and prefix_lens must not be NULL");
+  if (!aligned(bt->block_table, 4) || !aligned(bt->seq_lens, 4) ||
+      (!decode && (!aligned(bt->cu_seqlens_q, 4) || !aligned(bt->prefix_lens, 4))))
+    return fail(MXS_ELAYOUT, "int32 metadata must be 4-byte aligned");
+  if (bt->bt_width < NB)
+    return fail(MXS_ELAYOUT, "block table width %d is narrower than ceil(max_seq_len / page_size) = %lld",
+                bt->bt_width, (long long)NB);
+  if (bt->batch > 1 && bt->bt_row_stride < bt->bt_width)
+    return fail(MXS_ELAYOUT, "block table row stride %lld is smaller than its width %d", (long long)bt->bt_row_stride,
+                bt->bt_width);
+  // outputs
+  if (want_bs) {
+    int rc = check_out("block_scores", bs, rows, H, NB);
+    if (rc) return rc;
+  }
+  if (want_lg) {
+    int rc = check_out("logits", lg, rows, H, bt->max_seq_len);
+    if (rc) return rc;
+  }
+  // device and plan
+  int dev;
+  DeviceInfo info;
+  int rc = current_device(&dev, &info);
+  if (rc != MXS_OK) return rc;
+  mxs_plan plan;
+  if (plan_in) {
+    if (plan_in->mode != mode || plan_in->q_dtype != q->dtype || plan_in->page_size != P || plan_in->num_heads != H ||
+        plan_in->batch != bt->batch || plan_in->max_seq_len != bt->max_seq_len ||
+        (!decode && plan_in->max_query_len != bt->max_query_len) || plan_in->want_logits != (want_lg ? 1 : 0) ||
+        plan_in->want_blocks != (want_bs ? 1 : 0))
+      return fail(MXS_EINVAL, "the plan was made for different shapes or outputs");
+    plan = *plan_in;
+  } else {
+    rc = mxs_plan_make(mode, q->dtype, P, H, bt->batch, decode ? 1 : bt->max_query_len, bt->max_seq_len, want_lg,
+                       want_bs, 0, &plan);
+    if (rc != MXS_OK) return rc;
+  }
+  if (plan.items == 0) return MXS_OK;
+
+  mxs::KArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint8_t*>(q->ptr);
+  a.q_row_stride = q->row_stride * es;
+  a.q_head_stride = q->head_stride * es;
+  a.H = H;
+  a.kd = static_cast<const uint8_t*>(k->data);
+  a.kd_page_stride = k->data_page_stride;
+  a.ks = static_cast<const uint8_t*>(k->scale);
+  a.ks_page_stride = k->scale_page_stride;
+  a.bt = bt->block_table;
+  a.bt_stride = bt->bt_row_stride;
+  a.cu = bt->cu_seqlens_q;
+  a.seq = bt->seq_lens;
+  a.prefix = bt->prefix_lens;
+  a.B = bt->batch;
+  a.max_seq_len = bt->max_seq_len;
+  a.NB = (int32_t)NB;
+  a.sm_scale = sm_scale;
+  if (want_bs) {
+    a.bs = bs->ptr;
+    a.bs_row_stride = bs->row_stride;
+    a.bs_head_stride = bs->head_stride;
+    a.vec_bs = aligned(bs->ptr, 16) && bs->row_stride % 4 == 0 && bs->head_stride % 4 == 0;
+  }
+  if (want_lg) {
+    a.lg = lg->ptr;
+    a.lg_row_stride = lg->row_stride;
+    a.lg_head_stride = lg->head_stride;
+    a.vec_lg = aligned(lg->ptr, 16) && lg->row_stride % 4 == 0 && lg->head_stride % 4 == 0;
+  }
+  a.slots_per_item = plan.slots_per_item;
+  a.pages_per_item = plan.pages_per_item;
+  a.slot_items = plan.slot_items;
+  a.page_items = plan.page_items;
+  a.head_groups = plan.head_groups;
+  a.items = plan.items;
+  hipError_t e = mxs::launch(plan, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MXS_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  return MXS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxs_score_prefill(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                      const mxs_out* block_scores, const mxs_out* logits, const mxs_plan* plan, void* stream) {
+  return score(MXS_MODE_PREFILL, q, k, batch, sm_scale, block_scores, logits, plan, stream);
+}
+
+int mxs_score_decode(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                     const mxs_out* block_scores, const mxs_out* logits, const mxs_plan* plan, void* stream) {
+  return score(MXS_MODE_DECODE, q, k, batch, sm_scale, block_scores, logits, plan, stream);
+}
+
+int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
+                     const mxs_out* logits, const mxs_out* block_scores, const mxs_plan* plan, void* stream) {
+  return score(MXS_MODE_LOGITS, q, k, batch, sm_scale, block_scores, logits, plan, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal interface between the host entry points (mxs_api.cpp) and the
+// gfx950 kernels (mxs_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxscore.h"
+
+namespace mxs {
+
+// Kernel ids stored in mxs_plan::kernel.
+enum KernelId : int32_t {
+  KID_DECODE = 1,     // one wave per (request, head group, page chunk); K straight to registers
+  KID_PREFILL = 2,    // workgroup per (request, slot block, page chunk); K staged in LDS
+  KID_LOGITS = 3,     // logits-first tiling (query as MFMA A operand, tokens along lanes)
+};
+
+constexpr int kWaves = 4;           // waves per workgroup, every kernel
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPrefillTiles = 4;    // 16-slot query tiles per wave (prefill)
+constexpr int kLogitsTiles = 4;     // 16-slot query tiles per wave (logits)
+constexpr int kDecodeHeads = 64;    // heads per decode wave (4 tiles of 16)
+
+// Everything a kernel needs, by value. Byte strides for query and cache,
+// element strides for int32 tables and fp32 outputs.
+struct KArgs {
+  const uint8_t* q;
+  int64_t q_row_stride;     // bytes
+  int64_t q_head_stride;    // bytes
+  int32_t H;
+  const uint8_t* kd;
+  int64_t kd_page_stride;   // bytes
+  const uint8_t* ks;
+  int64_t ks_page_stride;   // bytes
+  const int32_t* bt;
+  int64_t bt_stride;        // elements
+  const int32_t* cu;        // prefill / logits
+  const int32_t* seq;
+  const int32_t* prefix;    // prefill / logits
+  int32_t B;
+  int32_t max_seq_len;
+  int32_t NB;
+  float sm_scale;
+  float* bs;                // block scores (may be null in logits mode)
+  int64_t bs_row_stride;
+  int64_t bs_head_stride;
+  float* lg;                // logits (may be null in prefill / decode)
+  int64_t lg_row_stride;
+  int64_t lg_head_stride;
+  int32_t slots_per_item;
+  int32_t pages_per_item;
+  int32_t slot_items;
+  int32_t page_items;
+  int32_t head_groups;
+  int64_t items;
+  int32_t vec_bs;           // block-score rows 16-byte aligned (vector stores allowed)
+  int32_t vec_lg;           // logit rows 16-byte aligned
+};
+
+// Launchers (mxs_kernels.hip). Return the HIP status of the launch.
+hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
+
+// Workgroups of `kernel` (for the given q dtype and page size) that fit on one CU.
+int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size);
+
+}  // namespace mxs

@@ -1,0 +1,392 @@
+// gfx950 kernels of the paged MXFP4 index scorer.
+//
+// One instruction does the arithmetic: v_mfma_scale_f32_16x16x128_f8f6f4
+// with the MXFP4 K tile as the fp4 operand, the e4m3 query tile as the fp8
+// operand, the token's e8m0 byte as the fp4 operand's block scale and 127
+// (x1) for the query (ATOM #2770, squashed pa_decode MXFP4 commit: one
+// scaled MFMA per 16 tokens x 16 queries, K e8m0 byte as scaleA). Operand
+// layout, measured on gfx950 with one-hot probes:
+//   fp4 operand, lane (g = lane/16, i = lane%16): row/column i, elements
+//     32g..32g+31, element 2m in the low nibble of byte m (16 bytes, 4 VGPRs);
+//   fp8 operand, lane (g, i): row/column i, elements 16g..16g+15 in bytes
+//     0..15 and 64+16g..64+16g+15 in bytes 16..31 (8 VGPRs), as the pages state;
+//   block scale, lane (g, i): scales elements 32g..32g+31 of row/column i;
+//   result C[16][16], lane (g, i) register v: C[4g + v][i].
+// An MXFP4 token row is therefore fed to the MFMA exactly as it sits in the
+// page: 16 contiguous bytes per lane, no dequantization (aiter #7061,
+// "Kernels": the page stays MXFP4 and is the fp4 A operand).
+//
+// Query rounding: bf16 -> f32 (exact) -> clamp to +-448 -> v_cvt_pk_fp8_f32
+// (round to nearest even, OCP e4m3 on gfx950). With the clamp this equals
+// round-to-nearest-even with saturation for every finite bf16 input
+// (checked exhaustively on gfx950); NaN stays NaN (aiter #7061, "Kernels").
+//
+// Scaling: logit = RN(RN(dot) * sm_scale); the block max is taken on the
+// unscaled dots and scaled afterwards, which gives the same bits because
+// sm_scale > 0 and rounding is monotone.
+#include <limits.h>
+
+#include "mxs_internal.h"
+
+namespace mxs {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float clamp_e4m3(float x) {
+  return (x != x) ? x : __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
+}
+
+// Four bf16 values (two dwords, element order low half first) -> four e4m3 bytes.
+__device__ __forceinline__ int bf16x4_to_e4m3(uint32_t w0, uint32_t w1) {
+  const float a = __builtin_bit_cast(float, w0 << 16);
+  const float b = __builtin_bit_cast(float, w0 & 0xFFFF0000u);
+  const float c = __builtin_bit_cast(float, w1 << 16);
+  const float d = __builtin_bit_cast(float, w1 & 0xFFFF0000u);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), r, true);
+  return r;
+}
+
+// The fp8-operand slice of one 128-element query vector held by lane group g:
+// elements 16g..16g+15 and 64+16g..64+16g+15. p == nullptr gives zeros
+// (padding lanes beyond the last head or row).
+template <int QDT>
+__device__ __forceinline__ v8i load_q_tile(const uint8_t* p, int g) {
+  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (p == nullptr) return r;
+  if constexpr (QDT == MXS_Q_E4M3) {
+    const u4 lo = *reinterpret_cast<const u4*>(p + 16 * g);
+    const u4 hi = *reinterpret_cast<const u4*>(p + 64 + 16 * g);
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  } else {
+    const u4* lo = reinterpret_cast<const u4*>(p + 32 * g);         // bf16 elements 16g..
+    const u4* hi = reinterpret_cast<const u4*>(p + 128 + 32 * g);   // bf16 elements 64+16g..
+    const u4 a0 = lo[0], a1 = lo[1], b0 = hi[0], b1 = hi[1];
+    r[0] = bf16x4_to_e4m3(a0[0], a0[1]); r[1] = bf16x4_to_e4m3(a0[2], a0[3]);
+    r[2] = bf16x4_to_e4m3(a1[0], a1[1]); r[3] = bf16x4_to_e4m3(a1[2], a1[3]);
+    r[4] = bf16x4_to_e4m3(b0[0], b0[1]); r[5] = bf16x4_to_e4m3(b0[2], b0[3]);
+    r[6] = bf16x4_to_e4m3(b1[0], b1[1]); r[7] = bf16x4_to_e4m3(b1[2], b1[3]);
+  }
+  return r;
+}
+
+// C[token][query] for 16 tokens (fp4 A: 16 bytes per lane, block scale kscale)
+// against 16 queries (fp8 B), fresh accumulator.
+__device__ __forceinline__ v4f mma_kq(u4 k, v8i q, int kscale) {
+  const v8i a = {(int)k[0], (int)k[1], (int)k[2], (int)k[3], 0, 0, 0, 0};
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q, z, 4, 0, 0, kscale, 0, 127);
+}
+
+__device__ __forceinline__ float max4(v4f c) {
+  return __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
+}
+
+// Max over the four lane groups (lanes i, i+16, i+32, i+48).
+__device__ __forceinline__ float fold_groups(float m) {
+  m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+  m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+  return m;
+}
+
+// Four consecutive logits starting at token t0 (a multiple of 4) of one
+// (row, head) output row, clipped to the window W.
+__device__ __forceinline__ void store_logits4(float* row, int t0, v4f v, int W, bool vec) {
+  if (vec && t0 + 3 < W) {
+    *reinterpret_cast<v4f*>(row + t0) = v;
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (t0 + x < W) row[t0 + x] = v[x];
+  }
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// ---------------------------------------------------------------------------
+// Decode: one wave per (request, group of 64 heads, chunk of pages). The
+// wave's K tiles come straight from HBM into registers (each page is read by
+// exactly one wave, so staging in LDS would buy nothing): per 16-token tile,
+// lane (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous
+// block per wave instruction) and the e8m0 byte g of that token.
+// ---------------------------------------------------------------------------
+template <int QDT, int P>
+__global__ void __launch_bounds__(kThreads) k_decode(KArgs a) {
+  constexpr int TPP = P / 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (item >= a.items) return;
+  const int hg = (int)(item % a.head_groups);
+  const int64_t rest = item / a.head_groups;
+  const int pc = (int)(rest % a.page_items);
+  const int b = (int)(rest / a.page_items);
+
+  const int limit = clampi(a.seq[b], 0, a.max_seq_len);
+  const int live_pages = (limit + P - 1) / P;
+  const int j0 = pc * a.pages_per_item;
+  const int j1 = min(j0 + a.pages_per_item, a.NB);
+  const int nq = min(4, (a.H - hg * kDecodeHeads + 15) / 16);
+
+  v8i qt[4];
+  int head[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int h = hg * kDecodeHeads + n * 16 + i;
+    head[n] = h < a.H ? h : -1;
+    const uint8_t* p = head[n] >= 0 ? a.q + (int64_t)b * a.q_row_stride + (int64_t)h * a.q_head_stride : nullptr;
+    qt[n] = load_q_tile<QDT>(p, g);
+  }
+  float* lrow[4];
+  float* brow[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    lrow[n] = (a.lg && head[n] >= 0) ? a.lg + (int64_t)b * a.lg_row_stride + (int64_t)head[n] * a.lg_head_stride : nullptr;
+    brow[n] = head[n] >= 0 ? a.bs + (int64_t)b * a.bs_row_stride + (int64_t)head[n] * a.bs_head_stride : nullptr;
+  }
+  const float s = a.sm_scale;
+
+  for (int j = j0; j < j1; ++j) {
+    float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    if (j < live_pages) {
+      const int64_t page = a.bt[(int64_t)b * a.bt_stride + j];
+      const uint8_t* dp = a.kd + page * a.kd_page_stride;
+      const uint8_t* sp = a.ks + page * a.ks_page_stride;
+      u4 kt[TPP];
+      int ksc[TPP];
+#pragma unroll
+      for (int t = 0; t < TPP; ++t) {
+        kt[t] = *reinterpret_cast<const u4*>(dp + (16 * t + i) * 64 + 16 * g);
+        ksc[t] = sp[(16 * t + i) * 4 + g];
+      }
+      const bool partial = (j + 1) * P > limit;
+#pragma unroll
+      for (int t = 0; t < TPP; ++t) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          if (n < nq) {
+            v4f c = mma_kq(kt[t], qt[n], ksc[t]);
+            if (partial) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (j * P + 16 * t + 4 * g + v >= limit) c[v] = kNegInf;
+            }
+            m[n] = __builtin_fmaxf(m[n], max4(c));
+            if (lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * s, a.max_seq_len, a.vec_lg);
+          }
+        }
+      }
+    } else if (a.lg) {
+      const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (lrow[n])
+#pragma unroll
+          for (int t = 0; t < TPP; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (n < nq) {
+        const float r = fold_groups(m[n]);
+        if (g == 0 && brow[n]) brow[n][j] = r * s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill (also the logits path for now): one workgroup per work item
+// (request, block of query slots, chunk of pages), looping over items with
+// a grid stride. A query slot is (row, head); slot = row * H + head, so a
+// 16-slot tile is 16 heads of one row when H is a multiple of 16. Each wave
+// keeps NQ query tiles in registers for the whole item; every page is staged
+// once per workgroup in LDS (double-buffered, 8.5 KB per buffer at P = 128)
+// and read by all four waves.
+// ---------------------------------------------------------------------------
+template <int P>
+struct PageStage {
+  static constexpr int kDataChunks = P * 64 / 16 / kThreads;   // 16-byte chunks per thread
+  u4 d[kDataChunks];
+  uint32_t sc;
+};
+
+template <int P>
+__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
+    st.d[c] = *reinterpret_cast<const u4*>(dp + 16 * (tid + kThreads * c));
+  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+}
+
+template <int P>
+__device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
+    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
+  if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
+}
+
+template <int QDT, int P, bool WANT_BS, bool WANT_LG>
+__global__ void __launch_bounds__(kThreads) k_prefill(KArgs a) {
+  constexpr int TPP = P / 16;
+  constexpr int NQ = kPrefillTiles;
+  constexpr int PB = P * 68;   // bytes of one staged page
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const float s = a.sm_scale;
+  const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
+
+  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int pc = (int)(item % a.page_items);
+    const int64_t rest = item / a.page_items;
+    const int sb = (int)(rest % a.slot_items);
+    const int b = (int)(rest / a.slot_items);
+    const int row0 = a.cu[b];
+    const int qlen = a.cu[b + 1] - row0;
+    const int64_t nslots = (int64_t)qlen * a.H;
+    const int64_t sbeg = (int64_t)sb * a.slots_per_item;
+    if (sbeg >= nslots) continue;   // uniform over the workgroup
+    const int seq = a.seq[b], pre = a.prefix[b];
+    const int64_t slast = min(sbeg + (int64_t)a.slots_per_item, nslots) - 1;
+    const int item_lim = clampi(min(seq, pre + (int)(slast / a.H) + 1), 0, a.max_seq_len);
+
+    // this lane's query slots
+    v8i qt[NQ];
+    int lim[NQ];
+    float* brow[NQ];
+    float* lrow[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int64_t sl = sbeg + (int64_t)(wave * NQ + n) * 16 + i;
+      const bool valid = sl < nslots;
+      const int r = valid ? (int)(sl / a.H) : 0;
+      const int h = valid ? (int)(sl % a.H) : 0;
+      const int64_t grow = (int64_t)row0 + r;
+      lim[n] = valid ? clampi(min(seq, pre + r + 1), 0, a.max_seq_len) : 0;
+      qt[n] = load_q_tile<QDT>(valid ? a.q + grow * a.q_row_stride + (int64_t)h * a.q_head_stride : nullptr, g);
+      brow[n] = (WANT_BS && valid) ? a.bs + grow * a.bs_row_stride + (int64_t)h * a.bs_head_stride : nullptr;
+      lrow[n] = (WANT_LG && valid) ? a.lg + grow * a.lg_row_stride + (int64_t)h * a.lg_head_stride : nullptr;
+    }
+    // smallest limit among this wave's slots: the limit of its first slot
+    const int64_t wfirst = sbeg + (int64_t)wave * NQ * 16;
+    const int wave_min_lim = wfirst < nslots ? clampi(min(seq, pre + (int)(wfirst / a.H) + 1), 0, a.max_seq_len) : 0;
+
+    const int j0 = pc * a.pages_per_item;
+    const int j1 = min(j0 + a.pages_per_item, a.NB);
+    const int jl = min(j1, (item_lim + P - 1) / P);   // pages [j0, jl) hold live tokens
+
+    if (j0 < jl) {
+      const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+      {
+        PageStage<P> st;
+        const int64_t page = btrow[j0];
+        stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+        stage_store<P>(st, lds, tid);
+      }
+      __syncthreads();
+      for (int j = j0; j < jl; ++j) {
+        const bool more = j + 1 < jl;
+        PageStage<P> nx;
+        if (more) {
+          const int64_t page = btrow[j + 1];
+          stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+        }
+        const uint8_t* kb = lds + ((j - j0) & 1) * PB;
+        float m[NQ];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
+        const bool need_mask = (j + 1) * P > wave_min_lim;
+#pragma unroll
+        for (int t = 0; t < TPP; ++t) {
+          const u4 kt = *reinterpret_cast<const u4*>(kb + (16 * t + i) * 64 + 16 * g);
+          const int ksc = kb[P * 64 + (16 * t + i) * 4 + g];
+#pragma unroll
+          for (int n = 0; n < NQ; ++n) {
+            v4f c = mma_kq(kt, qt[n], ksc);
+            if (need_mask) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (j * P + 16 * t + 4 * g + v >= lim[n]) c[v] = kNegInf;
+            }
+            m[n] = __builtin_fmaxf(m[n], max4(c));
+            if (WANT_LG && lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * s, a.max_seq_len, a.vec_lg);
+          }
+        }
+        if (more) stage_store<P>(nx, lds + ((j + 1 - j0) & 1) * PB, tid);
+        if (WANT_BS) {
+#pragma unroll
+          for (int n = 0; n < NQ; ++n) {
+            const float r = fold_groups(m[n]);
+            if (g == 0 && brow[n]) brow[n][j] = r * s;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // pages without a live token for any slot of this item
+    for (int j = max(j0, jl); j < j1; ++j) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        if (WANT_BS && g == 0 && brow[n]) brow[n][j] = kNegInf;
+        if (WANT_LG && lrow[n])
+#pragma unroll
+          for (int t = 0; t < TPP; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+      }
+    }
+  }
+}
+
+template <typename K>
+int occ_of(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), kThreads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int QDT, int P>
+hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  const dim3 grid(plan.grid), block(kThreads);
+  void* args[] = {const_cast<KArgs*>(&a)};
+  const void* fn = nullptr;
+  if (plan.kernel == KID_DECODE) {
+    fn = reinterpret_cast<const void*>(&k_decode<QDT, P>);
+  } else {
+    const bool bs = a.bs != nullptr, lg = a.lg != nullptr;
+    if (bs && lg) fn = reinterpret_cast<const void*>(&k_prefill<QDT, P, true, true>);
+    else if (bs) fn = reinterpret_cast<const void*>(&k_prefill<QDT, P, true, false>);
+    else fn = reinterpret_cast<const void*>(&k_prefill<QDT, P, false, true>);
+  }
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+template <int QDT, int P>
+int occupancy_qp(int32_t kernel) {
+  if (kernel == KID_DECODE) return occ_of(&k_decode<QDT, P>);
+  return occ_of(&k_prefill<QDT, P, true, false>);
+}
+
+}  // namespace
+
+hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  if (plan.q_dtype == MXS_Q_BF16) {
+    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
+  }
+  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+}
+
+int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size) {
+  if (q_dtype == MXS_Q_BF16)
+    return page_size == 128 ? occupancy_qp<MXS_Q_BF16, 128>(kernel) : occupancy_qp<MXS_Q_BF16, 64>(kernel);
+  return page_size == 128 ? occupancy_qp<MXS_Q_E4M3, 128>(kernel) : occupancy_qp<MXS_Q_E4M3, 64>(kernel);
+}
+
+}  // namespace mxs

@@ -1,0 +1,191 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the CPU
+oracle on the same seeded inputs, and compare under the documented rule.
+
+Comparison rule (per finite element):
+    |gpu - ref| <= max(2^-20 * |ref|, 2^-10 * sm_scale * M)
+where ref is the oracle's RN_fp32(sm_scale * exact dot) and M is the sum of
+|Q_hat[e] * K[e]| over the 128 elements (for a block score: the largest M
+among the page's live tokens). The first term is the relative bound asked
+for; the second is the measured error of the block-scaled MFMA under
+cancellation (groups of 8 elements keep about 12 bits below their largest
+product; worst measured 2^-11.95 * M), with a 4x margin. -inf positions,
+output indexing and the argmax over pages must match exactly (the argmax
+may differ only between values that are equal within the same bound).
+A floor on the fraction of bit-identical values guards against systematic
+drift that the per-element bound would let through.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import mxfp4_paged_cache_amd as mx
+from mxfp4_paged_cache_amd import workloads as W
+
+REL = 2.0 ** -20
+ABS_M = 2.0 ** -10
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def q_numpy(q: torch.Tensor):
+    """Query as numpy bit patterns: uint16 (bf16) or uint8 (e4m3); keeps strides."""
+    qc = q.cpu() if q.device.type != "cpu" else q
+    if qc.dtype == torch.bfloat16:
+        return qc.view(torch.int16).numpy().view(np.uint16), "bf16"
+    return qc.view(torch.uint8).numpy(), "e4m3"
+
+
+def oracle_run(inp: W.Inputs, *, rows=None, want_logits=True, want_blocks=True, table: int = 0,
+               max_seq_len: Optional[int] = None, sm_scale: float = W.INV_SQRT_D, compact: bool = False):
+    """Oracle on host copies of the inputs. ``compact`` gathers only the pages the
+    block table references (valid because page order is irrelevant, a pinned property)."""
+    wl = inp.wl
+    mode = "decode" if wl.mode == "decode" else "prefill"
+    qn, qdt = q_numpy(inp.q)
+    bt = inp.block_tables[table].cpu().numpy()
+    if compact:
+        if rows is not None:
+            # only the requests of the sampled rows are read
+            if mode == "decode":
+                need = np.unique(np.asarray(rows))
+            else:
+                cu = inp.cu_seqlens_q.cpu().numpy()
+                need = np.unique(np.searchsorted(cu, np.asarray(rows), side="right") - 1)
+            keep = np.zeros(bt.shape[0], bool)
+            keep[need] = True
+            bt = np.where(keep[:, None], bt, -1).astype(np.int32)
+        used = np.unique(bt[bt >= 0])
+        idx = torch.as_tensor(used, dtype=torch.long, device=inp.k_data.device)
+        kd = inp.k_data.index_select(0, idx).cpu().numpy()
+        ks = inp.k_scale.index_select(0, idx).cpu().numpy()
+        remap = np.full(int(bt.max()) + 1 if bt.size else 1, -1, np.int64)
+        remap[used] = np.arange(len(used))
+        bt = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    else:
+        kd = inp.k_data.cpu().numpy() if inp.k_data.device.type != "cpu" else inp.k_data.numpy()
+        ks = inp.k_scale.cpu().numpy() if inp.k_scale.device.type != "cpu" else inp.k_scale.numpy()
+    return oracle.score(mode=mode, q=qn, q_dtype=qdt, k_data=kd, k_scale=ks, page_size=wl.page_size,
+                        block_table=bt, seq_lens=inp.seq_lens.cpu().numpy(),
+                        max_seq_len=max_seq_len if max_seq_len is not None else wl.window, sm_scale=sm_scale,
+                        cu_seqlens_q=inp.cu_seqlens_q.cpu().numpy(), prefix_lens=inp.prefix_lens.cpu().numpy(),
+                        rows=rows, want_logits=want_logits, want_blocks=want_blocks, want_mags=True)
+
+
+def block_mags(mags: np.ndarray, P: int, NB: int) -> np.ndarray:
+    R, H, Wd = mags.shape
+    pad = NB * P - Wd
+    m = np.concatenate([mags, np.zeros((R, H, pad))], axis=2) if pad > 0 else mags[:, :, :NB * P]
+    return m.reshape(R, H, NB, P).max(axis=3)
+
+
+@dataclass
+class Stats:
+    n: int
+    finite: int
+    exact: float
+    within_rel: float
+    max_rel: float
+
+
+def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, *, what: str,
+            min_exact: float) -> Stats:
+    gpu = np.asarray(gpu, np.float32)
+    ref = np.asarray(ref, np.float32)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert not np.isnan(gpu).any(), f"{what}: NaN in GPU output"
+    assert np.array_equal(np.isneginf(gpu), np.isneginf(ref)), \
+        f"{what}: -inf pattern differs at {np.argwhere(np.isneginf(gpu) != np.isneginf(ref))[:5].tolist()}"
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(gpu)), f"{what}: finite pattern differs"
+    g = gpu[fin].astype(np.float64)
+    r = ref[fin].astype(np.float64)
+    m = mag[fin]
+    err = np.abs(g - r)
+    tol = np.maximum(REL * np.abs(r), ABS_M * sm_scale * m)
+    bad = err > tol
+    if bad.any():
+        k = np.argmax(err - tol)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {len(r)} values outside the bound; worst gpu={g[k]!r} "
+                             f"ref={r[k]!r} M={m[k]!r} tol={tol[k]!r}")
+    same = (g == r)
+    exact = float(same.mean()) if len(r) else 1.0
+    within = float((err <= REL * np.abs(r)).mean()) if len(r) else 1.0
+    max_rel = float(np.max(err / np.maximum(np.abs(r), 1e-300))) if len(r) else 0.0
+    st = Stats(gpu.size, int(fin.sum()), exact, within, max_rel)
+    say(f"  {what}: {st.finite}/{st.n} finite, bit-exact {exact:.6f}, within 2^-20 rel {within:.6f}, max rel {max_rel:.3g}")
+    assert exact >= min_exact, f"{what}: bit-exact fraction {exact:.6f} below floor {min_exact}"
+    return st
+
+
+def compare_argmax(gpu_bs: np.ndarray, ref_bs: np.ndarray, mag_b: np.ndarray, sm_scale: float, what: str):
+    """Argmax over pages (lowest index on ties, -1 when all -inf) must match,
+    unless the two candidates are equal within the comparison bound."""
+    def amax(x):
+        a = np.argmax(x, axis=-1)
+        allinf = np.all(np.isneginf(x), axis=-1)
+        return np.where(allinf, -1, a)
+    ag, ar = amax(gpu_bs), amax(ref_bs)
+    diff = np.argwhere(ag != ar)
+    for idx in diff:
+        idx = tuple(idx)
+        jg, jr = ag[idx], ar[idx]
+        assert jg >= 0 and jr >= 0, f"{what}: argmax differs on an all -inf row"
+        vg, vr = float(ref_bs[idx + (jg,)]), float(ref_bs[idx + (jr,)])
+        tol = max(REL * abs(vr), ABS_M * sm_scale * max(mag_b[idx + (jg,)], mag_b[idx + (jr,)])) * 2
+        assert abs(vg - vr) <= tol, f"{what}: argmax {jg} vs {jr} at {idx} is not a near tie ({vg} vs {vr})"
+    say(f"  {what}: argmax over pages equal on {ag.size - len(diff)}/{ag.size} (rest near ties)")
+
+
+def gpu_inputs(inp: W.Inputs) -> W.Inputs:
+    """Copy host-generated inputs to the GPU (same bytes, same layout)."""
+    dev = torch.device("cuda")
+    out = W.Inputs(wl=inp.wl, q=_to_dev(inp.q, dev), k_data=None, k_scale=None,
+                   block_tables=[t.to(dev) for t in inp.block_tables], cu_seqlens_q=inp.cu_seqlens_q.to(dev),
+                   seq_lens=inp.seq_lens.to(dev), prefix_lens=inp.prefix_lens.to(dev))
+    if inp.region is not None:
+        region = inp.region.to(dev)
+        out.region = region
+        out.k_data = torch.as_strided(region, inp.k_data.shape, inp.k_data.stride(), inp.k_data.storage_offset())
+        out.k_scale = torch.as_strided(region, inp.k_scale.shape, inp.k_scale.stride(), inp.k_scale.storage_offset())
+    else:
+        out.k_data = inp.k_data.to(dev)
+        out.k_scale = inp.k_scale.to(dev)
+    return out
+
+
+def _to_dev(t: torch.Tensor, dev) -> torch.Tensor:
+    if t.is_contiguous():
+        return t.to(dev)
+    base = t._base if t._base is not None else t
+    b = base.to(dev)
+    return torch.as_strided(b, t.shape, t.stride(), t.storage_offset())
+
+
+def run_gpu(inp: W.Inputs, *, table: int = 0, want_logits=None, plan=None, sm_scale: float = W.INV_SQRT_D,
+            max_seq_len: Optional[int] = None):
+    wl = inp.wl
+    msl = max_seq_len if max_seq_len is not None else wl.window
+    bt = inp.block_tables[table]
+    if wl.mode == "decode":
+        r = mx.score_decode(inp.q, inp.k_data, inp.k_scale, bt, inp.seq_lens, msl, sm_scale,
+                            logits=bool(wl.want_logits if want_logits is None else want_logits), plan=plan)
+        return (r if isinstance(r, tuple) else (r, None))
+    if wl.mode == "logits":
+        r = mx.score_logits(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                            max(wl.q_lens), msl, sm_scale, block_scores=wl.want_blocks, plan=plan)
+        if isinstance(r, tuple):
+            return r[1], r[0]
+        return None, r
+    r = mx.score_prefill(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                         max(wl.q_lens) if wl.q_lens else 0, msl, sm_scale,
+                         logits=bool(wl.want_logits if want_logits is None else want_logits), plan=plan)
+    return (r if isinstance(r, tuple) else (r, None))

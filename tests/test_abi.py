@@ -1,0 +1,190 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, validates arguments before any device work, and plans purely from
+host integers (aiter #5518, decode auto-CTA: host-known buckets, graph-stable).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_paged_cache_amd as mx
+from mxfp4_paged_cache_amd import build as mxbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxscore.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.library_path()):
+        mxbuild.build(force=True)
+    return mx.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_library_agree(L):
+    names = declared_functions()
+    assert set(names) == set(mx.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in mxscore.h but not exported"
+
+
+def test_exports_are_c_symbols():
+    out = os.popen(f"nm -D --defined-only {mx.library_path()}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_version(L):
+    assert b"gfx950" in L.mxs_version()
+
+
+# ------------------------------------------------------------------ validation
+
+FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced: every case below fails validation first
+
+
+def valid_args(mode=mx.MXS_MODE_PREFILL):
+    q = mx.Query(FAKE, mx.MXS_Q_BF16, 64 * 128, 128, 64)
+    k = mx.KCache(FAKE + 0x100000, 8704, FAKE + 0x100000 + 8192, 8704, 128, 16)
+    b = mx.Batch(FAKE + 0x200000, 16, 16, FAKE + 0x300000, FAKE + 0x300100, FAKE + 0x300200, 1, 64, 64, 1024)
+    bs = mx.Out(FAKE + 0x400000, 64 * 8, 8)
+    lg = mx.Out(None, 0, 0)
+    return q, k, b, bs, lg
+
+
+def call(L, q, k, b, bs, lg, sm=0.0883883, fn="mxs_score_prefill"):
+    f = getattr(L, fn)
+    return f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(b), ctypes.c_float(sm), ctypes.byref(bs),
+             ctypes.byref(lg), None, None)
+
+
+CASES = [
+    ("fp16 query dtype", lambda q, k, b, bs, lg: setattr(q, "dtype", 3), mx.MXS_EDTYPE),
+    ("zero heads", lambda q, k, b, bs, lg: setattr(q, "num_heads", 0), mx.MXS_EINVAL),
+    ("page size 32", lambda q, k, b, bs, lg: setattr(k, "page_size", 32), mx.MXS_ELAYOUT),
+    ("misaligned query rows", lambda q, k, b, bs, lg: setattr(q, "row_stride", 64 * 128 + 4), mx.MXS_ELAYOUT),
+    ("misaligned query base", lambda q, k, b, bs, lg: setattr(q, "ptr", FAKE + 8), mx.MXS_ELAYOUT),
+    ("narrow data view", lambda q, k, b, bs, lg: setattr(k, "data_page_stride", 4096), mx.MXS_ELAYOUT),
+    ("narrow scale view", lambda q, k, b, bs, lg: setattr(k, "scale_page_stride", 256), mx.MXS_ELAYOUT),
+    ("misaligned data view", lambda q, k, b, bs, lg: setattr(k, "data", FAKE + 0x100004), mx.MXS_ELAYOUT),
+    ("misaligned scale view", lambda q, k, b, bs, lg: setattr(k, "scale", FAKE + 0x100002), mx.MXS_ELAYOUT),
+    ("no pages", lambda q, k, b, bs, lg: setattr(k, "num_pages", 0), mx.MXS_EINVAL),
+    ("narrow block table", lambda q, k, b, bs, lg: setattr(b, "bt_width", 7), mx.MXS_ELAYOUT),
+    ("null block table", lambda q, k, b, bs, lg: setattr(b, "block_table", None), mx.MXS_EINVAL),
+    ("null seq_lens", lambda q, k, b, bs, lg: setattr(b, "seq_lens", None), mx.MXS_EINVAL),
+    ("null prefix_lens", lambda q, k, b, bs, lg: setattr(b, "prefix_lens", None), mx.MXS_EINVAL),
+    ("negative batch", lambda q, k, b, bs, lg: setattr(b, "batch", -1), mx.MXS_EINVAL),
+    ("no block_scores", lambda q, k, b, bs, lg: setattr(bs, "ptr", None), mx.MXS_EINVAL),
+    ("narrow output rows", lambda q, k, b, bs, lg: setattr(bs, "head_stride", 4), mx.MXS_ELAYOUT),
+    ("misaligned output", lambda q, k, b, bs, lg: setattr(bs, "ptr", FAKE + 0x400002), mx.MXS_ELAYOUT),
+    ("null query", lambda q, k, b, bs, lg: setattr(q, "ptr", None), mx.MXS_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", CASES, ids=[c[0] for c in CASES])
+def test_rejections_before_device_work(L, name, mutate, code):
+    q, k, b, bs, lg = valid_args()
+    mutate(q, k, b, bs, lg)
+    assert call(L, q, k, b, bs, lg) == code, L.mxs_last_error()
+    assert L.mxs_last_error()
+
+
+@pytest.mark.parametrize("sm", [0.0, -1.0, float("nan"), float("inf")])
+def test_rejects_bad_sm_scale(L, sm):
+    q, k, b, bs, lg = valid_args()
+    assert call(L, q, k, b, bs, lg, sm=sm) == mx.MXS_EINVAL
+
+
+def test_logits_mode_needs_logits(L):
+    q, k, b, bs, lg = valid_args()
+    assert call(L, q, k, b, lg, bs, fn="mxs_score_logits") == mx.MXS_EINVAL
+
+
+def test_empty_problem_is_a_no_op(L):
+    # nothing to write: returns OK without touching any pointer or the device
+    q, k, b, bs, lg = valid_args()
+    b.total_rows = 0
+    assert call(L, q, k, b, bs, lg) == mx.MXS_OK
+    q, k, b, bs, lg = valid_args()
+    b.max_seq_len = 0
+    assert call(L, q, k, b, bs, lg) == mx.MXS_OK
+
+
+def test_no_device_is_reported():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a HIP device is visible; this case only runs without one")
+    L = mx.lib()
+    q, k, b, bs, lg = valid_args()
+    assert call(L, q, k, b, bs, lg) == mx.MXS_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ planning
+
+def plan_for(L, mode, *, H=64, P=128, B=64, mql=1, msl=131072, lg=0, bs=1, pun=0, cus=256, occ=3, dt=mx.MXS_Q_BF16):
+    p = mx.Plan()
+    rc = L.mxs_plan_make_for(mode, dt, P, H, B, mql, msl, lg, bs, pun, cus, occ, ctypes.byref(p))
+    return rc, p
+
+
+def test_plan_is_pure(L):
+    for mode, kw in [(mx.MXS_MODE_DECODE, {}), (mx.MXS_MODE_PREFILL, dict(B=1, mql=4096)),
+                     (mx.MXS_MODE_LOGITS, dict(B=8, mql=128, msl=8192, P=64, lg=1, bs=0))]:
+        rc1, p1 = plan_for(L, mode, **kw)
+        rc2, p2 = plan_for(L, mode, **kw)
+        assert rc1 == rc2 == 0
+        assert bytes(p1) == bytes(p2)
+
+
+def test_decode_plan_covers_every_page_once(L):
+    for B, msl, occ in [(64, 131072, 3), (1, 8192, 3), (4, 1000, 2), (3, 0, 1)]:
+        rc, p = plan_for(L, mx.MXS_MODE_DECODE, B=B, msl=msl, occ=occ)
+        assert rc == 0
+        NB = (msl + 127) // 128
+        assert p.page_items * p.pages_per_item >= NB
+        assert (p.page_items - 1) * p.pages_per_item < max(NB, 1)
+        assert p.items == B * p.head_groups * p.page_items
+        assert p.grid * 4 >= p.items
+
+
+def test_prefill_plan_covers_every_slot(L):
+    for B, mql, H, msl in [(1, 4096, 64, 131072), (1, 32768, 64, 132768), (3, 17, 2, 300), (8, 128, 64, 8192)]:
+        rc, p = plan_for(L, mx.MXS_MODE_PREFILL, B=B, mql=mql, H=H, msl=msl)
+        assert rc == 0
+        assert p.slot_items * p.slots_per_item >= mql * H
+        assert p.page_items * p.pages_per_item >= (msl + 127) // 128
+        assert p.items == B * p.slot_items * p.page_items
+        assert 1 <= p.grid <= max(p.items, 1)
+
+
+def test_parallel_unit_override(L):
+    rc, p = plan_for(L, mx.MXS_MODE_PREFILL, B=1, mql=4096, pun=100)
+    assert rc == 0 and p.grid == 100
+    rc, p = plan_for(L, mx.MXS_MODE_DECODE, pun=512)
+    assert rc == 0 and abs(p.grid - 512) <= 64
+
+
+def test_plan_rejections(L):
+    assert plan_for(L, 9)[0] == mx.MXS_EINVAL
+    assert plan_for(L, mx.MXS_MODE_DECODE, P=32)[0] == mx.MXS_ELAYOUT
+    assert plan_for(L, mx.MXS_MODE_DECODE, dt=5)[0] == mx.MXS_EDTYPE
+    assert plan_for(L, mx.MXS_MODE_DECODE, H=0)[0] == mx.MXS_EINVAL
+    assert plan_for(L, mx.MXS_MODE_LOGITS, lg=0)[0] == mx.MXS_EINVAL
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 1, 128), dtype=torch.bfloat16)
+    kd = torch.zeros((1, 128, 64), dtype=torch.uint8)
+    ks = torch.zeros((1, 128, 4), dtype=torch.uint8)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd, ks, bt, sl, 128, 0.1)

@@ -1,0 +1,360 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Comparison rule in tests/gpu_helpers.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp4_paged_cache_amd as mx
+from mxfp4_paged_cache_amd import workloads as W
+from tests.gpu_helpers import (block_mags, compare, compare_argmax, gpu_inputs, oracle_run, run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+S = W.INV_SQRT_D
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.lib()   # fails loudly when the HIP library is missing
+    oracle.build()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_case(wl: W.Workload, *, seed=0, min_exact=0.999, q_strided=False, want_logits=None):
+    say(f"case {wl.name} seed={seed} P={wl.page_size} H={wl.H} q={wl.q_dtype} B={wl.B} mode={wl.mode}")
+    host = W.make_inputs(wl, seed, "cpu", q_strided=q_strided)
+    dev = gpu_inputs(host)
+    lg_on = wl.want_logits if want_logits is None else want_logits
+    bs, lg = run_gpu(dev, want_logits=lg_on)
+    torch.cuda.synchronize()
+    ref = oracle_run(host, want_logits=True, want_blocks=True)
+    NB = wl.NB
+    mb = block_mags(ref.mags, wl.page_size, NB)
+    if bs is not None:
+        compare(bs.cpu().numpy(), ref.blocks, mb, S, what="block scores", min_exact=min_exact)
+        compare_argmax(bs.cpu().numpy(), ref.blocks, mb, S, "block scores")
+    if lg is not None:
+        compare(lg.cpu().numpy(), ref.logits, ref.mags, S, what="logits", min_exact=min_exact)
+    return host, dev, bs, lg, ref
+
+
+def test_prefill_64_rows_ctx1k():
+    # 64 rows after a 960-token prefix, ctx 1024, H=64, P=128, 16-page pool:
+    # logits and block scores (the small prefill workload).
+    check_case(W.prefill_small(), seed=1)
+
+
+@pytest.mark.parametrize("P", [64, 128])
+@pytest.mark.parametrize("qdt", ["bf16", "e4m3"])
+def test_decode_ragged(P, qdt):
+    wl = W.Workload("decode_ragged", "decode", H=64, page_size=P, q_lens=[1] * 5, prefix_lens=[0] * 5,
+                    seq_lens=[1000, 128, 1, 0, 300], q_dtype=qdt, want_logits=True, max_seq_len=1030)
+    check_case(wl, seed=2)
+
+
+@pytest.mark.parametrize("H", [1, 2, 3, 17, 64])
+@pytest.mark.parametrize("P", [64, 128])
+def test_prefill_ragged_heads(H, P):
+    # mixed query lengths with an empty request, prefixes mid-page, heads that
+    # are not a multiple of the 16-slot tile (tiles straddle rows)
+    wl = W.Workload("prefill_ragged", "prefill", H=H, page_size=P, q_lens=[5, 0, 17, 1], prefix_lens=[70, 3, 100, 0],
+                    seq_lens=[75, 3, 117, 1], want_logits=True, max_seq_len=200)
+    check_case(wl, seed=3 + H)
+
+
+def test_prefill_e4m3_query_long_rows():
+    wl = W.Workload("prefill_e4m3", "prefill", H=64, page_size=128, q_lens=[40], prefix_lens=[2000],
+                    seq_lens=[2040], q_dtype="e4m3", want_logits=True)
+    check_case(wl, seed=4)
+
+
+def test_wide_scale_bytes():
+    # e8m0 bytes 100..150 (outside the e4m3-exact window [119, 133])
+    wl = W.Workload("prefill_wide_scales", "prefill", H=64, page_size=128, q_lens=[24], prefix_lens=[700],
+                    seq_lens=[724], scale_lo=100, scale_hi=150, want_logits=True)
+    check_case(wl, seed=5, min_exact=0.60)
+
+
+def test_logits_shared_region_small():
+    # two-slot shared region, slot 1 scored, 64-token pages, padded table rows,
+    # window not a multiple of the page size
+    wl = W.Workload("logits_shared_small", "logits", H=64, page_size=64, q_lens=[20, 7], prefix_lens=[480, 0],
+                    seq_lens=[500, 7], want_logits=True, want_blocks=True, layout="shared", shared_first_page=5,
+                    table_pad=3, max_seq_len=530)
+    check_case(wl, seed=6)
+
+
+def test_strided_query():
+    wl = W.Workload("prefill_strided_q", "prefill", H=16, page_size=128, q_lens=[9], prefix_lens=[250],
+                    seq_lens=[259], want_logits=True)
+    check_case(wl, seed=7, q_strided=True)
+
+
+def test_e4m3_conversion_exhaustive():
+    # Every bf16 pattern through the real path: query element 0 = pattern,
+    # K = 1.0 at element 0, scale 2^0, sm_scale 1 -> the logit is the e4m3
+    # value the kernel rounded the pattern to; compare with the oracle's table.
+    T, H = 1024, 64
+    q = torch.zeros((T, H, 128), dtype=torch.int16)
+    q[:, :, 0] = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(T, H)
+    q = q.view(torch.bfloat16).cuda()
+    kd = torch.zeros((1, 128, 64), dtype=torch.uint8)
+    kd[0, 0, 0] = 0x02
+    ks = torch.full((1, 128, 4), 127, dtype=torch.uint8)
+    kd, ks = kd.cuda(), ks.cuda()
+    bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    sl = torch.tensor([1], dtype=torch.int32, device="cuda")
+    pl = torch.tensor([0], dtype=torch.int32, device="cuda")
+    bs, lg = mx.score_prefill(q, kd, ks, bt, cu, sl, pl, T, 1, 1.0, logits=True)
+    got = lg[:, :, 0].reshape(-1).cpu().numpy()
+    table = oracle.bf16_to_e4m3_table()
+    ref = np.array([oracle.e4m3_value(int(b)) for b in table])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan].astype(np.float32))   # +0 and -0 compare equal
+    say(f"  all {65536 - nan.sum()} non-NaN bf16 patterns round exactly as the oracle")
+
+
+def test_cross_mode_bitwise():
+    # decode == prefill with one row per request (prefix = seq_len - 1) ==
+    # logits mode, element for element; block score == max of the logits.
+    seq = [700, 129, 64, 1]
+    B = len(seq)
+    wd = W.Workload("xm_decode", "decode", H=64, page_size=128, q_lens=[1] * B, prefix_lens=[s - 1 for s in seq],
+                    seq_lens=seq, want_logits=True, max_seq_len=768)
+    host = W.make_inputs(wd, 8, "cpu")
+    dev = gpu_inputs(host)
+    bs_d, lg_d = run_gpu(dev, want_logits=True)
+    dev.wl = W.Workload("xm_prefill", "prefill", H=64, page_size=128, q_lens=[1] * B,
+                        prefix_lens=[s - 1 for s in seq], seq_lens=seq, want_logits=True, max_seq_len=768)
+    bs_p, lg_p = run_gpu(dev, want_logits=True)
+    dev.wl = W.Workload("xm_logits", "logits", H=64, page_size=128, q_lens=[1] * B,
+                        prefix_lens=[s - 1 for s in seq], seq_lens=seq, want_logits=True, want_blocks=True,
+                        max_seq_len=768)
+    bs_l, lg_l = run_gpu(dev)
+    torch.cuda.synchronize()
+    for a, b_, n in [(bs_d, bs_p, "decode/prefill blocks"), (bs_d, bs_l, "decode/logits blocks"),
+                     (lg_d, lg_p, "decode/prefill logits"), (lg_d, lg_l, "decode/logits logits")]:
+        assert torch.equal(a.view(torch.int32), b_.view(torch.int32)), n
+    mx_of_logits = lg_d.view(B, 64, 6, 128).amax(dim=3)
+    assert torch.equal(mx_of_logits, bs_d)
+
+
+def test_split_and_region_layouts_bitwise():
+    wl = W.Workload("region", "prefill", H=64, page_size=128, q_lens=[8, 3], prefix_lens=[300, 40],
+                    seq_lens=[308, 43], want_logits=True, layout="region")
+    host = W.make_inputs(wl, 9, "cpu")
+    dev_region = gpu_inputs(host)
+    dev_split = gpu_inputs(host)
+    dev_split.k_data = host.k_data.contiguous().cuda()
+    dev_split.k_scale = host.k_scale.contiguous().cuda()
+    dev_split.region = None
+    a = run_gpu(dev_region)
+    b = run_gpu(dev_split)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_explicit_plans_give_identical_outputs():
+    wl = W.Workload("plans", "prefill", H=64, page_size=128, q_lens=[33, 12], prefix_lens=[900, 100],
+                    seq_lens=[933, 112])
+    host = W.make_inputs(wl, 10, "cpu")
+    dev = gpu_inputs(host)
+    base, _ = run_gpu(dev)
+    for pun in (1, 7, 64, 1000):
+        p = mx.make_plan("prefill", torch.bfloat16, 128, 64, 2, 33, 933, False, True, pun)
+        other, _ = run_gpu(dev, plan=p)
+        assert torch.equal(base.view(torch.int32), other.view(torch.int32)), pun
+    wd = W.Workload("plans_d", "decode", H=64, page_size=64, q_lens=[1] * 3, prefix_lens=[0] * 3,
+                    seq_lens=[4000, 10, 2500])
+    host = W.make_inputs(wd, 11, "cpu")
+    dev = gpu_inputs(host)
+    base, _ = run_gpu(dev)
+    for pun in (1, 5, 300):
+        p = mx.make_plan("decode", torch.bfloat16, 64, 64, 3, 1, 4000, False, True, pun)
+        other, _ = run_gpu(dev, plan=p)
+        assert torch.equal(base.view(torch.int32), other.view(torch.int32)), pun
+
+
+def test_graph_replay_with_poisoned_outputs():
+    # Captured decode and prefill calls are replayed with outputs poisoned
+    # (NaN) in between; every replay must rewrite every element (aiter #5518,
+    # "Correctness": graph replay with logical outputs poisoned between replays).
+    wd = W.Workload("g_decode", "decode", H=64, page_size=128, q_lens=[1] * 3, prefix_lens=[0] * 3,
+                    seq_lens=[900, 5, 0], want_logits=True, max_seq_len=1024)
+    wp = W.Workload("g_prefill", "prefill", H=64, page_size=128, q_lens=[6, 2], prefix_lens=[500, 0],
+                    seq_lens=[506, 2], want_logits=True)
+    hd, hp = W.make_inputs(wd, 12, "cpu"), W.make_inputs(wp, 13, "cpu")
+    dd, dp = gpu_inputs(hd), gpu_inputs(hp)
+    bs_d = torch.empty((3, 64, 8), device="cuda")
+    lg_d = torch.empty((3, 64, 1024), device="cuda")
+    bs_p = torch.empty((8, 64, 4), device="cuda")
+    lg_p = torch.empty((8, 64, 506), device="cuda")
+    pd = mx.make_plan("decode", torch.bfloat16, 128, 64, 3, 1, 1024, True, True)
+    pp = mx.make_plan("prefill", torch.bfloat16, 128, 64, 2, 6, 506, True, True)
+
+    def step():
+        mx.score_decode(dd.q, dd.k_data, dd.k_scale, dd.block_table, dd.seq_lens, 1024, S, out=bs_d, logits=lg_d,
+                        plan=pd)
+        mx.score_prefill(dp.q, dp.k_data, dp.k_scale, dp.block_table, dp.cu_seqlens_q, dp.seq_lens, dp.prefix_lens,
+                         6, 506, S, out=bs_p, logits=lg_p, plan=pp)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (bs_d, lg_d, bs_p, lg_p)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (bs_d, lg_d, bs_p, lg_p):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip((bs_d, lg_d, bs_p, lg_p), eager):
+            assert torch.equal(t.view(torch.int32), e.view(torch.int32)), rep
+    say("  4 replays with poisoned outputs equal the eager result")
+
+
+def test_rejections_on_gpu_tensors():
+    dev = "cuda"
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device=dev)
+    kd = torch.zeros((3, 128, 64), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((3, 128, 4), dtype=torch.uint8, device=dev)
+    bt = torch.zeros((2, 2), dtype=torch.int32, device=dev)
+    sl = torch.tensor([100, 200], dtype=torch.int32, device=dev)
+    ok = mx.score_decode(q, kd, ks, bt, sl, 256, S)
+    assert ok.shape == (2, 4, 2)
+    with pytest.raises(ValueError):
+        mx.score_decode(q.half(), kd, ks, bt, sl, 256, S)                     # fp16 query
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd[:, :, :32], ks, bt, sl, 256, S)                 # narrow data view
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd, ks[:2], bt, sl, 256, S)                        # page counts differ
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd, ks, bt[:, :1], sl, 256, S)                     # narrow block table
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd, ks, bt, torch.tensor([100, 0, 200, 0], dtype=torch.int32, device=dev)[::2], 256, S)
+    big = torch.zeros((2, 4, 132), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        mx.score_decode(big[:, :, :128], kd, ks, bt, sl, 256, S)             # misaligned query rows
+    with pytest.raises(ValueError):
+        mx.score_decode(q, kd, ks, bt, sl, 256, float("nan"))
+    cu = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    pl = torch.tensor([0, 0], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        mx.score_prefill(q, kd, ks, bt, cu, sl, pl, 1, 256, S, out=torch.empty((2, 4, 3), device=dev))
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled oracle)
+
+def _limits(wl: W.Workload) -> torch.Tensor:
+    return torch.tensor(wl.limits(), dtype=torch.int64)
+
+
+def _check_block_mask_full(bs: torch.Tensor, wl: W.Workload):
+    lim = _limits(wl).to(bs.device)
+    live_pages = (lim + wl.page_size - 1) // wl.page_size
+    j = torch.arange(bs.shape[2], device=bs.device)
+    expect_fin = (j[None, :] < live_pages[:, None])[:, None, :].expand_as(bs)
+    assert not torch.isnan(bs).any()
+    assert torch.equal(torch.isfinite(bs), expect_fin)
+    assert torch.equal(torch.isneginf(bs), ~expect_fin)
+
+
+def _sample_rows(wl: W.Workload, extra: int, seed: int):
+    T = wl.T
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1}
+    lim = wl.limits()
+    P = wl.page_size
+    for r in range(1, T):   # rows whose limit crosses a page boundary
+        if lim[r] // P != lim[r - 1] // P:
+            rows.add(r)
+            if len(rows) > 4:
+                break
+    rows |= set(int(x) for x in rng.integers(0, T, extra))
+    return np.array(sorted(rows), np.int32)
+
+
+def test_full_decode_b64_ctx128k():
+    wl = W.decode_b64_128k()
+    say(f"case {wl.name}: generating inputs on the GPU")
+    inp = W.make_inputs(wl, 20, "cuda")
+    bs, _ = run_gpu(inp)
+    torch.cuda.synchronize()
+    _check_block_mask_full(bs, wl)
+    rows = np.array([0, 37, 63], np.int32)
+    ref = oracle_run(inp, rows=rows, want_logits=True, compact=True)
+    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    got = bs[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
+    compare(got, ref.blocks, mb, S, what="decode block scores (3 sampled requests)", min_exact=0.999)
+    compare_argmax(got, ref.blocks, mb, S, "decode block scores")
+
+
+def test_full_prefill_q4096_ctx128k_e4m3():
+    wl = W.prefill_long()
+    say(f"case {wl.name}: generating inputs on the GPU")
+    inp = W.make_inputs(wl, 21, "cuda")
+    bs, _ = run_gpu(inp)
+    torch.cuda.synchronize()
+    _check_block_mask_full(bs, wl)
+    rows = _sample_rows(wl, 3, 21)
+    ref = oracle_run(inp, rows=rows, want_logits=True, compact=True)
+    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    got = bs[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
+    compare(got, ref.blocks, mb, S, what=f"prefill block scores ({len(rows)} sampled rows)", min_exact=0.999)
+    compare_argmax(got, ref.blocks, mb, S, "prefill block scores")
+    del bs, inp
+    torch.cuda.empty_cache()
+
+
+def test_full_chunked_prefill_32k_wide_scales():
+    wl = W.prefill_chunk()
+    say(f"case {wl.name}: generating inputs on the GPU")
+    inp = W.make_inputs(wl, 22, "cuda")
+    bs, _ = run_gpu(inp)
+    torch.cuda.synchronize()
+    _check_block_mask_full(bs, wl)
+    rows = _sample_rows(wl, 2, 22)
+    ref = oracle_run(inp, rows=rows, want_logits=True, compact=True)
+    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    got = bs[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
+    compare(got, ref.blocks, mb, S, what=f"chunked prefill block scores ({len(rows)} sampled rows)", min_exact=0.60)
+    compare_argmax(got, ref.blocks, mb, S, "chunked prefill block scores")
+    del bs, inp
+    torch.cuda.empty_cache()
+
+
+def test_full_logits_shared_pool_past_4p6gb():
+    wl = W.logits_shared_pool()
+    say(f"case {wl.name}: generating the 4.6 GB shared region on the GPU")
+    inp = W.make_inputs(wl, 23, "cuda")
+    first = int(inp.block_table[inp.block_table >= 0].min()) * inp.k_data.stride(0) + inp.k_data.storage_offset()
+    assert first >= 4_608_000_000
+    _, lg = run_gpu(inp)
+    torch.cuda.synchronize()
+    lim = _limits(wl).cuda()
+    t = torch.arange(wl.window, device="cuda")
+    expect_fin = (t[None, :] < lim[:, None])[:, None, :].expand_as(lg)
+    assert not torch.isnan(lg).any()
+    assert torch.equal(torch.isfinite(lg), expect_fin)
+    rows = np.array([0, 127, 128, 700, 1023], np.int32)
+    ref = oracle_run(inp, rows=rows, want_logits=True, want_blocks=False, compact=True)
+    got = lg[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
+    compare(got, ref.logits, ref.mags, S, what="logits past 4.608e9 B (5 sampled rows)", min_exact=0.999)
+    del lg, inp
+    torch.cuda.empty_cache()
