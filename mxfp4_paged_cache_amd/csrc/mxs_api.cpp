@@ -149,6 +149,7 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     int64_t target_waves = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * mxs::kWaves : capacity * mxs::kWaves;
     int64_t chunks = lanes > 0 ? ceil_div(target_waves, lanes) : 1;
     if (chunks > NB) chunks = NB;
+    if (chunks < ceil_div(NB, mxs::kDecodeMaxPages)) chunks = ceil_div(NB, mxs::kDecodeMaxPages);
     if (chunks < 1) chunks = 1;
     p.pages_per_item = (int32_t)(NB > 0 ? ceil_div(NB, chunks) : 1);
     p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, p.pages_per_item) : 1);

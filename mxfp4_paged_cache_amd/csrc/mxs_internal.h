@@ -21,6 +21,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefillTiles = 4;    // 16-slot query tiles per wave (prefill)
 constexpr int kLogitsTiles = 4;     // 16-slot query tiles per wave (logits)
 constexpr int kDecodeHeads = 64;    // heads per decode wave (4 tiles of 16)
+constexpr int kDecodeMaxPages = 32; // pages per decode wave (ids fit one VGPR; scores staged in LDS)
+constexpr int kDecodeStageStride = kDecodeMaxPages + 1;   // LDS row pitch in floats (odd: no bank conflicts)
 
 // Everything a kernel needs, by value. Byte strides for query and cache,
 // element strides for int32 tables and fp32 outputs.

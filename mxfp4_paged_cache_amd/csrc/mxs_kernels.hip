@@ -52,6 +52,9 @@ __device__ __forceinline__ int bf16x4_to_e4m3(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+template <int QDT>
+__device__ __forceinline__ v8i load_q_slice(const uint8_t* p, int g);
+
 // The fp8-operand slice of one 128-element query vector held by lane group g:
 // elements 16g..16g+15 and 64+16g..64+16g+15. p == nullptr gives zeros
 // (padding lanes beyond the last head or row).
@@ -59,6 +62,12 @@ template <int QDT>
 __device__ __forceinline__ v8i load_q_tile(const uint8_t* p, int g) {
   v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
   if (p == nullptr) return r;
+  return load_q_slice<QDT>(p, g);
+}
+
+template <int QDT>
+__device__ __forceinline__ v8i load_q_slice(const uint8_t* p, int g) {
+  v8i r;
   if constexpr (QDT == MXS_Q_E4M3) {
     const u4 lo = *reinterpret_cast<const u4*>(p + 16 * g);
     const u4 hi = *reinterpret_cast<const u4*>(p + 64 + 16 * g);
@@ -88,6 +97,12 @@ __device__ __forceinline__ float max4(v4f c) {
   return __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
 }
 
+// running max m over the four values of one MFMA result
+// (compiles to two v_max3_f32; the compiler inserts the MFMA-to-VALU wait states)
+__device__ __forceinline__ float max_into(float m, v4f c) {
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m, c[0]), c[1]), __builtin_fmaxf(c[2], c[3]));
+}
+
 // Max over the four lane groups (lanes i, i+16, i+32, i+48).
 __device__ __forceinline__ float fold_groups(float m) {
   m = __builtin_fmaxf(m, __shfl_xor(m, 16));
@@ -110,18 +125,102 @@ __device__ __forceinline__ void store_logits4(float* row, int t0, v4f v, int W, 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // ---------------------------------------------------------------------------
-// Decode: one wave per (request, group of 64 heads, chunk of pages). The
-// wave's K tiles come straight from HBM into registers (each page is read by
-// exactly one wave, so staging in LDS would buy nothing): per 16-token tile,
-// lane (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous
-// block per wave instruction) and the e8m0 byte g of that token.
+// Decode: one wave per (request, group of 64 heads, chunk of <= 64 pages).
+// Each page is read by exactly one wave, so K goes straight from HBM into
+// registers (staging it in LDS would buy nothing): per 16-token tile, lane
+// (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
+// per wave instruction) and e8m0 byte g of that token. Pages are double-
+// buffered in registers: the loads of page j+2 are in flight while page j+1
+// is scored. The chunk's page ids are read once into one VGPR (lane l holds
+// the id of page j0 + l) and picked per page with readlane.
 // ---------------------------------------------------------------------------
-template <int QDT, int P>
-__global__ void __launch_bounds__(kThreads) k_decode(KArgs a) {
+template <int P>
+struct RegPage {
+  u4 d[P / 16];
+  int s[P / 16];
+};
+
+// One page into registers. dp/sp are the page's (uniform) bases; doff/soff the
+// lane's byte offsets inside the page (data: 64 i + 16 g; scale: 4 i + g).
+template <int P>
+__device__ __forceinline__ void load_reg_page(RegPage<P>& kp, const uint8_t* dp, const uint8_t* sp, uint32_t doff,
+                                              uint32_t soff) {
+#pragma unroll
+  for (int t = 0; t < P / 16; ++t) {
+    kp.d[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 1024u * t));
+    kp.s[t] = __builtin_nontemporal_load(sp + soff + 64u * t);
+  }
+}
+
+// Query tile for lane (g, i) of head h (a padding lane reads a valid head and
+// zeroes the result, so the load itself is never divergent).
+template <int QDT>
+__device__ __forceinline__ v8i load_q_tile_masked(const uint8_t* p, int g, bool valid) {
+  v8i r = load_q_slice<QDT>(p, g);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) r[d] = valid ? r[d] : 0;
+  return r;
+}
+
+// Score one register-resident page against the wave's four query tiles.
+// MASK: the page holds the end of the live window (tokens >= lip are dead).
+// The tile loop is software-pipelined by hand: the four MFMAs of tile t are
+// issued before the results of tile t-1 are folded, and a scheduling fence
+// after each step keeps only two tiles of results live.
+template <int P, bool MASK, bool LG>
+__device__ __forceinline__ void decode_page(const RegPage<P>& kp, const v8i (&qt)[4], int j, int lip, int g,
+                                            const bool (&hv)[4], float* stage, int jrel, float* lg_row,
+                                            const int64_t (&hoff)[4], const KArgs& a) {
+  constexpr int TPP = P / 16;
+  const float s = a.sm_scale;
+  float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  v4f prev[4];
+  const int lrel = lip - 4 * g;   // token 16 tp + 4 g + v is live iff 16 tp + v < lrel
+#pragma unroll
+  for (int t = 0; t <= TPP; ++t) {
+    v4f cur[4];
+    if (t < TPP) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) cur[n] = mma_kq(kp.d[t], qt[n], kp.s[t]);
+    }
+    if (t > 0) {
+      const int tp = t - 1;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        v4f c = prev[n];
+        if constexpr (MASK) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) c[v] = (16 * tp + v < lrel) ? c[v] : kNegInf;
+        }
+        m[n] = max_into(m[n], c);
+        if constexpr (LG) {
+          if (hv[n])
+            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * tp + 4 * g, c * s, a.max_seq_len,
+                          a.vec_lg);
+        }
+      }
+    }
+    if (t < TPP) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) prev[n] = cur[n];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const float r = fold_groups(m[n]);
+    if (g == 0) stage[(16 * n + (threadIdx.x & 15)) * kDecodeStageStride + jrel] = r * s;
+  }
+}
+
+template <int QDT, int P, bool LG>
+__global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   constexpr int TPP = P / 16;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, i = lane & 15;
-  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // the wave index is uniform across the wave: keep everything derived from it scalar
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
   if (item >= a.items) return;
   const int hg = (int)(item % a.head_groups);
   const int64_t rest = item / a.head_groups;
@@ -132,71 +231,83 @@ __global__ void __launch_bounds__(kThreads) k_decode(KArgs a) {
   const int live_pages = (limit + P - 1) / P;
   const int j0 = pc * a.pages_per_item;
   const int j1 = min(j0 + a.pages_per_item, a.NB);
-  const int nq = min(4, (a.H - hg * kDecodeHeads + 15) / 16);
+  const int jl = min(j1, live_pages);                 // pages [j0, jl) are scored
 
   v8i qt[4];
-  int head[4];
+  bool hv[4];
+  int64_t hoff[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int h = hg * kDecodeHeads + n * 16 + i;
-    head[n] = h < a.H ? h : -1;
-    const uint8_t* p = head[n] >= 0 ? a.q + (int64_t)b * a.q_row_stride + (int64_t)h * a.q_head_stride : nullptr;
-    qt[n] = load_q_tile<QDT>(p, g);
+    hv[n] = h < a.H;
+    const int hc = hv[n] ? h : a.H - 1;
+    hoff[n] = (int64_t)hc;
+    qt[n] = load_q_tile_masked<QDT>(a.q + (int64_t)b * a.q_row_stride + (int64_t)hc * a.q_head_stride, g, hv[n]);
   }
-  float* lrow[4];
-  float* brow[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    lrow[n] = (a.lg && head[n] >= 0) ? a.lg + (int64_t)b * a.lg_row_stride + (int64_t)head[n] * a.lg_head_stride : nullptr;
-    brow[n] = head[n] >= 0 ? a.bs + (int64_t)b * a.bs_row_stride + (int64_t)head[n] * a.bs_head_stride : nullptr;
-  }
-  const float s = a.sm_scale;
+  float* bs_row = a.bs + (int64_t)b * a.bs_row_stride;
+  float* lg_row = LG ? a.lg + (int64_t)b * a.lg_row_stride : nullptr;
+  // this wave's staging area for its block scores: [64 heads][pages of the chunk]
+  __shared__ float stage_all[kWaves][kDecodeHeads * kDecodeStageStride];
+  float* stage = stage_all[wave];
 
-  for (int j = j0; j < j1; ++j) {
-    float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-    if (j < live_pages) {
-      const int64_t page = a.bt[(int64_t)b * a.bt_stride + j];
-      const uint8_t* dp = a.kd + page * a.kd_page_stride;
-      const uint8_t* sp = a.ks + page * a.ks_page_stride;
-      u4 kt[TPP];
-      int ksc[TPP];
-#pragma unroll
-      for (int t = 0; t < TPP; ++t) {
-        kt[t] = *reinterpret_cast<const u4*>(dp + (16 * t + i) * 64 + 16 * g);
-        ksc[t] = sp[(16 * t + i) * 4 + g];
-      }
-      const bool partial = (j + 1) * P > limit;
-#pragma unroll
-      for (int t = 0; t < TPP; ++t) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          if (n < nq) {
-            v4f c = mma_kq(kt[t], qt[n], ksc[t]);
-            if (partial) {
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (j * P + 16 * t + 4 * g + v >= limit) c[v] = kNegInf;
-            }
-            m[n] = __builtin_fmaxf(m[n], max4(c));
-            if (lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * s, a.max_seq_len, a.vec_lg);
-          }
-        }
-      }
-    } else if (a.lg) {
-      const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        if (lrow[n])
-#pragma unroll
-          for (int t = 0; t < TPP; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+  if (j0 < jl) {
+    const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+    const int my_page = (j0 + lane < jl) ? btrow[j0 + lane] : 0;
+    const uint32_t doff = (uint32_t)(i * 64 + 16 * g);
+    const uint32_t soff = (uint32_t)(i * 4 + g);
+    auto load_page = [&](RegPage<P>& kp, int j) {
+      const int jj = min(j, jl - 1);
+      const int64_t page = __builtin_amdgcn_readlane(my_page, jj - j0);
+      load_reg_page<P>(kp, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, doff, soff);
+    };
+    auto score = [&](const RegPage<P>& kp, int j) {
+      const int lip = limit - j * P;                 // live tokens in this page
+      if (lip >= P)
+        decode_page<P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+      else
+        decode_page<P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+    };
+    RegPage<P> A, B;
+    load_page(A, j0);
+    load_page(B, j0 + 1);
+    // the fences stop the scheduler from hoisting a refill above the scoring
+    // of the buffer it overwrites (that would keep three pages live)
+    for (int j = j0; j < jl; j += 2) {
+      score(A, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(A, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < jl) score(B, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(B, j + 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  // pages past the live window: -inf
+  for (int j = max(j0, jl); j < j1; ++j) {
+    if (g == 0)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) stage[(16 * n + i) * kDecodeStageStride + (j - j0)] = kNegInf;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      if (n < nq) {
-        const float r = fold_groups(m[n]);
-        if (g == 0 && brow[n]) brow[n][j] = r * s;
+      if (hv[n]) {
+        if constexpr (LG) {
+          const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+          for (int t = 0; t < TPP; ++t)
+            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+        }
       }
     }
+  }
+  // Block scores leave LDS as one contiguous run of (j1 - j0) floats per head:
+  // consecutive lanes write consecutive pages, so every store instruction
+  // covers whole cache lines instead of 64 scattered 4-byte words.
+  const int npg = j1 - j0;
+  const int nh = min(kDecodeHeads, a.H - hg * kDecodeHeads);
+  for (int idx = lane; idx < nh * npg; idx += 64) {
+    const int h = idx / npg, p = idx - h * npg;
+    bs_row[(int64_t)(hg * kDecodeHeads + h) * a.bs_head_stride + j0 + p] = stage[h * kDecodeStageStride + p];
   }
 }
 
@@ -239,7 +350,7 @@ __global__ void __launch_bounds__(kThreads) k_prefill(KArgs a) {
   constexpr int PB = P * 68;   // bytes of one staged page
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PB];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   const float s = a.sm_scale;
   const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
@@ -358,7 +469,7 @@ hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<KArgs*>(&a)};
   const void* fn = nullptr;
   if (plan.kernel == KID_DECODE) {
-    fn = reinterpret_cast<const void*>(&k_decode<QDT, P>);
+    fn = a.lg ? reinterpret_cast<const void*>(&k_decode<QDT, P, true>) : reinterpret_cast<const void*>(&k_decode<QDT, P, false>);
   } else {
     const bool bs = a.bs != nullptr, lg = a.lg != nullptr;
     if (bs && lg) fn = reinterpret_cast<const void*>(&k_prefill<QDT, P, true, true>);
@@ -370,7 +481,7 @@ hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
 
 template <int QDT, int P>
 int occupancy_qp(int32_t kernel) {
-  if (kernel == KID_DECODE) return occ_of(&k_decode<QDT, P>);
+  if (kernel == KID_DECODE) return occ_of(&k_decode<QDT, P, false>);
   return occ_of(&k_prefill<QDT, P, true, false>);
 }
 
