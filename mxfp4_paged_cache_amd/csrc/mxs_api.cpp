@@ -168,6 +168,10 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     const int64_t base = (int64_t)batch * p.slot_items;
     const int64_t want_items = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * 4 : capacity * 4;
     int64_t chunks = base > 0 ? ceil_div(want_items, base) : 1;
+    // Page chunks in multiples of 8 (when there are pages enough): with a grid
+    // that is also a multiple of 8, workgroup c only sees chunks c mod 8, so
+    // each of the 8 XCDs reads one eighth of the pages into its own L2.
+    if (NB >= 8) chunks = ceil_div(chunks, 8) * 8;
     if (chunks > NB) chunks = NB;
     if (chunks < 1) chunks = 1;
     int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
@@ -175,6 +179,7 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, ppi) : 1);
     p.items = base * p.page_items;
     int64_t grid = parallel_unit_num > 0 ? parallel_unit_num : capacity;
+    if (parallel_unit_num <= 0 && grid >= 8) grid = grid / 8 * 8;
     if (grid > p.items) grid = p.items;
     if (grid < 1) grid = 1;
     p.grid = (int32_t)grid;

@@ -233,6 +233,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   const int j1 = min(j0 + a.pages_per_item, a.NB);
   const int jl = min(j1, live_pages);                 // pages [j0, jl) are scored
 
+  // the chunk's page ids first (lane l: page j0 + l), so their latency overlaps the query loads
+  const int my_page = (j0 + lane < jl) ? a.bt[(int64_t)b * a.bt_stride + j0 + lane] : 0;
   v8i qt[4];
   bool hv[4];
   int64_t hoff[4];
@@ -251,8 +253,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   float* stage = stage_all[wave];
 
   if (j0 < jl) {
-    const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
-    const int my_page = (j0 + lane < jl) ? btrow[j0 + lane] : 0;
     const uint32_t doff = (uint32_t)(i * 64 + 16 * g);
     const uint32_t soff = (uint32_t)(i * 4 + g);
     auto load_page = [&](RegPage<P>& kp, int j) {
@@ -313,12 +313,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill (also the logits path for now): one workgroup per work item
-// (request, block of query slots, chunk of pages), looping over items with
-// a grid stride. A query slot is (row, head); slot = row * H + head, so a
-// 16-slot tile is 16 heads of one row when H is a multiple of 16. Each wave
-// keeps NQ query tiles in registers for the whole item; every page is staged
+// (request, block of 256 query slots, chunk of pages), looping over items
+// with a grid stride. A query slot is (row, head); slot = row * H + head, so
+// a 16-slot tile is 16 heads of one row when H is a multiple of 16. Each wave
+// keeps 4 query tiles in registers for the whole item; every page is staged
 // once per workgroup in LDS (double-buffered, 8.5 KB per buffer at P = 128)
-// and read by all four waves.
+// and read by all four waves. Block scores are staged in LDS for up to 32
+// pages and leave as contiguous per-slot rows.
+//
+// Work items are ordered page chunk fastest. With a grid and a chunk count
+// that are both multiples of 8, workgroup c only ever sees chunks c mod 8;
+// workgroups are dispatched round-robin over the 8 XCDs, so each XCD reads
+// one eighth of the pages and keeps them in its own L2.
 // ---------------------------------------------------------------------------
 template <int P>
 struct PageStage {
@@ -343,12 +349,75 @@ __device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf
   if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
 }
 
-template <int QDT, int P, bool WANT_BS, bool WANT_LG>
-__global__ void __launch_bounds__(kThreads) k_prefill(KArgs a) {
+constexpr int kPrefillStagePages = 32;                      // pages per block-score flush
+constexpr int kPrefillStageStride = kPrefillStagePages + 1; // LDS row pitch (odd: no bank conflicts)
+constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;  // query slots per work item
+
+// Score one LDS-resident page against this wave's query tiles; r[n] gets the
+// (unscaled) max over the page's live tokens for slot (tile n, lane i).
+// The 16-token tiles run in a real loop, two per trip with two sets of
+// results, so at most two tiles of MFMA results are live: tile t's MFMAs are
+// issued, the next tile is read from LDS, then tile t-1 is folded.
+template <int P, bool MASK, bool LG>
+__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[kPrefillTiles],
+                                             const int (&lrel)[kPrefillTiles], int j, int g, int i,
+                                             float (&r)[kPrefillTiles], float* const (&lrow)[kPrefillTiles],
+                                             const KArgs& a) {
   constexpr int TPP = P / 16;
   constexpr int NQ = kPrefillTiles;
+  const uint8_t* kdl = kb + i * 64 + 16 * g;      // this lane's 16 bytes of tile t: kdl + 1024 t
+  const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
+  float m[NQ];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
+  auto mma = [&](u4 k, int sc, v4f (&c)[NQ]) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) c[n] = mma_kq(k, qt[n], sc);
+  };
+  auto fold = [&](int t, const v4f (&cc)[NQ]) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      v4f c = cc[n];
+      if constexpr (MASK) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel[n]) ? c[v] : kNegInf;
+      }
+      m[n] = max_into(m[n], c);
+      if constexpr (LG) {
+        if (lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * a.sm_scale, a.max_seq_len, a.vec_lg);
+      }
+    }
+  };
+  v4f cA[NQ], cB[NQ];
+  u4 k0 = *reinterpret_cast<const u4*>(kdl);
+  int s0 = ksl[0];
+  u4 k1 = *reinterpret_cast<const u4*>(kdl + 1024);
+  int s1 = ksl[64];
+  mma(k0, s0, cA);                                         // tile 0
+#pragma unroll 1
+  for (int t = 1; t < TPP - 1; t += 2) {
+    mma(k1, s1, cB);                                       // tile t
+    k0 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 1));
+    s0 = ksl[64 * (t + 1)];
+    fold(t - 1, cA);
+    mma(k0, s0, cA);                                       // tile t + 1
+    k1 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 2));
+    s1 = ksl[64 * (t + 2)];
+    fold(t, cB);
+  }
+  mma(k1, s1, cB);                                         // tile TPP - 1
+  fold(TPP - 2, cA);
+  fold(TPP - 1, cB);
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
+}
+
+template <int QDT, int P, bool WANT_BS, bool WANT_LG>
+__global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
+  constexpr int NQ = kPrefillTiles;
   constexpr int PB = P * 68;   // bytes of one staged page
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PB];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
+  __shared__ float stage[WANT_BS ? kPrefillSlots * kPrefillStageStride : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
@@ -363,27 +432,26 @@ __global__ void __launch_bounds__(kThreads) k_prefill(KArgs a) {
     const int row0 = a.cu[b];
     const int qlen = a.cu[b + 1] - row0;
     const int64_t nslots = (int64_t)qlen * a.H;
-    const int64_t sbeg = (int64_t)sb * a.slots_per_item;
+    const int64_t sbeg = (int64_t)sb * kPrefillSlots;
     if (sbeg >= nslots) continue;   // uniform over the workgroup
     const int seq = a.seq[b], pre = a.prefix[b];
-    const int64_t slast = min(sbeg + (int64_t)a.slots_per_item, nslots) - 1;
+    const int64_t slast = min(sbeg + (int64_t)kPrefillSlots, nslots) - 1;
     const int item_lim = clampi(min(seq, pre + (int)(slast / a.H) + 1), 0, a.max_seq_len);
 
     // this lane's query slots
     v8i qt[NQ];
     int lim[NQ];
-    float* brow[NQ];
     float* lrow[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       const int64_t sl = sbeg + (int64_t)(wave * NQ + n) * 16 + i;
       const bool valid = sl < nslots;
-      const int r = valid ? (int)(sl / a.H) : 0;
-      const int h = valid ? (int)(sl % a.H) : 0;
+      const int64_t slc = valid ? sl : nslots - 1;
+      const int r = (int)(slc / a.H);
+      const int h = (int)(slc % a.H);
       const int64_t grow = (int64_t)row0 + r;
       lim[n] = valid ? clampi(min(seq, pre + r + 1), 0, a.max_seq_len) : 0;
-      qt[n] = load_q_tile<QDT>(valid ? a.q + grow * a.q_row_stride + (int64_t)h * a.q_head_stride : nullptr, g);
-      brow[n] = (WANT_BS && valid) ? a.bs + grow * a.bs_row_stride + (int64_t)h * a.bs_head_stride : nullptr;
+      qt[n] = load_q_tile_masked<QDT>(a.q + grow * a.q_row_stride + (int64_t)h * a.q_head_stride, g, valid);
       lrow[n] = (WANT_LG && valid) ? a.lg + grow * a.lg_row_stride + (int64_t)h * a.lg_head_stride : nullptr;
     }
     // smallest limit among this wave's slots: the limit of its first slot
@@ -393,63 +461,67 @@ __global__ void __launch_bounds__(kThreads) k_prefill(KArgs a) {
     const int j0 = pc * a.pages_per_item;
     const int j1 = min(j0 + a.pages_per_item, a.NB);
     const int jl = min(j1, (item_lim + P - 1) / P);   // pages [j0, jl) hold live tokens
+    const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
 
     if (j0 < jl) {
-      const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
-      {
-        PageStage<P> st;
-        const int64_t page = btrow[j0];
-        stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
-        stage_store<P>(st, lds, tid);
-      }
-      __syncthreads();
-      for (int j = j0; j < jl; ++j) {
+      PageStage<P> st;
+      const int64_t page = btrow[j0];
+      stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+      stage_store<P>(st, kbuf, tid);
+    }
+    __syncthreads();
+    int jbase = j0;
+    for (int j = j0; j < j1; ++j) {
+      float r[NQ];
+      if (j < jl) {
         const bool more = j + 1 < jl;
         PageStage<P> nx;
         if (more) {
           const int64_t page = btrow[j + 1];
           stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
         }
-        const uint8_t* kb = lds + ((j - j0) & 1) * PB;
-        float m[NQ];
+        const uint8_t* kb = kbuf + ((j - j0) & 1) * PB;
+        int lrel[NQ];
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
-        const bool need_mask = (j + 1) * P > wave_min_lim;
+        for (int n = 0; n < NQ; ++n) lrel[n] = lim[n] - j * P - 4 * g;
+        if ((j + 1) * P > wave_min_lim)
+          prefill_page<P, true, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+        else
+          prefill_page<P, false, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+        if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
+      } else {
 #pragma unroll
-        for (int t = 0; t < TPP; ++t) {
-          const u4 kt = *reinterpret_cast<const u4*>(kb + (16 * t + i) * 64 + 16 * g);
-          const int ksc = kb[P * 64 + (16 * t + i) * 4 + g];
+        for (int n = 0; n < NQ; ++n) r[n] = kNegInf;
+        if constexpr (WANT_LG) {
 #pragma unroll
-          for (int n = 0; n < NQ; ++n) {
-            v4f c = mma_kq(kt, qt[n], ksc);
-            if (need_mask) {
+          for (int n = 0; n < NQ; ++n)
+            if (lrow[n])
 #pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (j * P + 16 * t + 4 * g + v >= lim[n]) c[v] = kNegInf;
-            }
-            m[n] = __builtin_fmaxf(m[n], max4(c));
-            if (WANT_LG && lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * s, a.max_seq_len, a.vec_lg);
-          }
+              for (int t = 0; t < P / 16; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
         }
-        if (more) stage_store<P>(nx, lds + ((j + 1 - j0) & 1) * PB, tid);
-        if (WANT_BS) {
-#pragma unroll
-          for (int n = 0; n < NQ; ++n) {
-            const float r = fold_groups(m[n]);
-            if (g == 0 && brow[n]) brow[n][j] = r * s;
-          }
-        }
-        __syncthreads();
       }
-    }
-    // pages without a live token for any slot of this item
-    for (int j = max(j0, jl); j < j1; ++j) {
+      if constexpr (WANT_BS) {
+        if (g == 0) {
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        if (WANT_BS && g == 0 && brow[n]) brow[n][j] = kNegInf;
-        if (WANT_LG && lrow[n])
-#pragma unroll
-          for (int t = 0; t < TPP; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+          for (int n = 0; n < NQ; ++n) stage[((wave * NQ + n) * 16 + i) * kPrefillStageStride + (j - jbase)] = r[n] * s;
+        }
+      }
+      __syncthreads();
+      if constexpr (WANT_BS) {
+        if (j - jbase == kPrefillStagePages - 1 || j == j1 - 1) {
+          // flush pages [jbase, j]: consecutive threads write consecutive pages of a slot row
+          const int npg = j - jbase + 1;
+          const int nvalid = (int)min((int64_t)kPrefillSlots, nslots - sbeg);
+          for (int idx = tid; idx < nvalid * npg; idx += kThreads) {
+            const int sl = idx / npg, p = idx - sl * npg;
+            const int64_t slot = sbeg + sl;
+            const int64_t grow = (int64_t)row0 + slot / a.H;
+            a.bs[grow * a.bs_row_stride + (slot % a.H) * a.bs_head_stride + jbase + p] =
+                stage[sl * kPrefillStageStride + p];
+          }
+          __syncthreads();
+          jbase = j + 1;
+        }
       }
     }
   }
