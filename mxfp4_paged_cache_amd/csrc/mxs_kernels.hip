@@ -37,8 +37,14 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Saturate to the largest finite e4m3 magnitude; NaN stays NaN. The NaN test
+// is on the bits: this file is compiled without NaN semantics for float
+// arithmetic (so the max folds need no quieting copies), and the only NaN
+// that can reach the kernels is an out-of-contract query element.
 __device__ __forceinline__ float clamp_e4m3(float x) {
-  return (x != x) ? x : __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
+  return nan ? x : __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
 }
 
 // Four bf16 values (two dwords, element order low half first) -> four e4m3 bytes.
@@ -341,11 +347,18 @@ __device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, 
   if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
 }
 
+// LDS layout of a staged page: the data of 16-token tile t is stored as
+// [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
+// a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
+// scales follow as [token][4 bytes] at P * 64.
 template <int P>
 __device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
 #pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
-    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
+    const int chunk = tid + kThreads * c;             // 16-byte chunk of the page: token chunk/4, group chunk%4
+    const int tok = chunk >> 2, grp = chunk & 3;
+    *reinterpret_cast<u4*>(buf + (tok >> 4) * 1024 + grp * 256 + (tok & 15) * 16) = st.d[c];
+  }
   if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
 }
 
@@ -365,7 +378,7 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
                                              const KArgs& a) {
   constexpr int TPP = P / 16;
   constexpr int NQ = kPrefillTiles;
-  const uint8_t* kdl = kb + i * 64 + 16 * g;      // this lane's 16 bytes of tile t: kdl + 1024 t
+  const uint8_t* kdl = kb + g * 256 + i * 16;     // this lane's 16 bytes of tile t: kdl + 1024 t
   const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
   float m[NQ];
 #pragma unroll
