@@ -175,6 +175,7 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     if (chunks > NB) chunks = NB;
     if (chunks < 1) chunks = 1;
     int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
+    if (ppi > 4) ppi = ceil_div(ppi, 4) * 4;   // chunk starts stay 16-byte aligned in the score rows
     p.pages_per_item = (int32_t)ppi;
     p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, ppi) : 1);
     p.items = base * p.page_items;

@@ -106,7 +106,7 @@ __device__ __forceinline__ float max4(v4f c) {
 // running max m over the four values of one MFMA result
 // (compiles to two v_max3_f32; the compiler inserts the MFMA-to-VALU wait states)
 __device__ __forceinline__ float max_into(float m, v4f c) {
-  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m, c[0]), c[1]), __builtin_fmaxf(c[2], c[3]));
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m, c[0]), c[1]), c[2]), c[3]);
 }
 
 // Max over the four lane groups (lanes i, i+16, i+32, i+48).
@@ -339,26 +339,29 @@ struct PageStage {
   uint32_t sc;
 };
 
-template <int P>
-__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
-#pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
-    st.d[c] = *reinterpret_cast<const u4*>(dp + 16 * (tid + kThreads * c));
-  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
-}
-
 // LDS layout of a staged page: the data of 16-token tile t is stored as
 // [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
 // a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
-// scales follow as [token][4 bytes] at P * 64.
+// scales follow as [token][4 bytes] at P * 64. Thread tid fills LDS slot
+// s = tid + 256 c (16 bytes, contiguous writes) with global bytes
+// 16 g..16 g+15 of token 16 t + i, (t, g, i) = (s / 64, s / 16 % 4, s % 16):
+// a wave still loads one contiguous 1 KB tile per instruction.
+template <int P>
+__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
+    const int sl = tid + kThreads * c;
+    const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
+    st.d[c] = *reinterpret_cast<const u4*>(dp + off);
+  }
+  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+}
+
 template <int P>
 __device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
 #pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
-    const int chunk = tid + kThreads * c;             // 16-byte chunk of the page: token chunk/4, group chunk%4
-    const int tok = chunk >> 2, grp = chunk & 3;
-    *reinterpret_cast<u4*>(buf + (tok >> 4) * 1024 + grp * 256 + (tok & 15) * 16) = st.d[c];
-  }
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
+    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
   if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
 }
 
@@ -368,9 +371,8 @@ constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;  // query slots per w
 
 // Score one LDS-resident page against this wave's query tiles; r[n] gets the
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
-// The 16-token tiles run in a real loop, two per trip with two sets of
-// results, so at most two tiles of MFMA results are live: tile t's MFMAs are
-// issued, the next tile is read from LDS, then tile t-1 is folded.
+// The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
+// most two tiles of MFMA results are live.
 template <int P, bool MASK, bool LG>
 __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[kPrefillTiles],
                                              const int (&lrel)[kPrefillTiles], int j, int g, int i,
@@ -401,26 +403,26 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
       }
     }
   };
-  v4f cA[NQ], cB[NQ];
+  // two tiles per trip, no MFMA result carried across trips; the next pair of
+  // K tiles is read from LDS while this pair is multiplied and folded
   u4 k0 = *reinterpret_cast<const u4*>(kdl);
   int s0 = ksl[0];
   u4 k1 = *reinterpret_cast<const u4*>(kdl + 1024);
   int s1 = ksl[64];
-  mma(k0, s0, cA);                                         // tile 0
 #pragma unroll 1
-  for (int t = 1; t < TPP - 1; t += 2) {
-    mma(k1, s1, cB);                                       // tile t
-    k0 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 1));
-    s0 = ksl[64 * (t + 1)];
-    fold(t - 1, cA);
-    mma(k0, s0, cA);                                       // tile t + 1
-    k1 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 2));
-    s1 = ksl[64 * (t + 2)];
-    fold(t, cB);
+  for (int t = 0; t < TPP; t += 2) {
+    v4f cA[NQ], cB[NQ];
+    mma(k0, s0, cA);
+    mma(k1, s1, cB);
+    if (t + 2 < TPP) {
+      k0 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 2));
+      s0 = ksl[64 * (t + 2)];
+      k1 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 3));
+      s1 = ksl[64 * (t + 3)];
+    }
+    fold(t, cA);
+    fold(t + 1, cB);
   }
-  mma(k1, s1, cB);                                         // tile TPP - 1
-  fold(TPP - 2, cA);
-  fold(TPP - 1, cB);
 #pragma unroll
   for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
 }
@@ -522,15 +524,26 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       __syncthreads();
       if constexpr (WANT_BS) {
         if (j - jbase == kPrefillStagePages - 1 || j == j1 - 1) {
-          // flush pages [jbase, j]: consecutive threads write consecutive pages of a slot row
+          // flush pages [jbase, j]: 8 threads per slot row, 4 pages per thread,
+          // so each group of 8 threads writes one contiguous run of the row
           const int npg = j - jbase + 1;
           const int nvalid = (int)min((int64_t)kPrefillSlots, nslots - sbeg);
-          for (int idx = tid; idx < nvalid * npg; idx += kThreads) {
-            const int sl = idx / npg, p = idx - sl * npg;
-            const int64_t slot = sbeg + sl;
-            const int64_t grow = (int64_t)row0 + slot / a.H;
-            a.bs[grow * a.bs_row_stride + (slot % a.H) * a.bs_head_stride + jbase + p] =
-                stage[sl * kPrefillStageStride + p];
+          const int part = tid & 7;
+          const bool vec = a.vec_bs && (jbase & 3) == 0 && 4 * part + 3 < npg;
+          for (int sl = tid >> 3; sl < nvalid; sl += kThreads / 8) {
+            if (4 * part >= npg) continue;
+            const uint32_t slot = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H)) + (uint32_t)sl;  // slot - H * row(sbeg)
+            const uint32_t dr = slot / (uint32_t)a.H;
+            const int64_t grow = (int64_t)row0 + sbeg / a.H + dr;
+            float* dst = a.bs + grow * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride + jbase +
+                         4 * part;
+            const float* src = stage + sl * kPrefillStageStride + 4 * part;
+            if (vec) {
+              const v4f v = {src[0], src[1], src[2], src[3]};
+              *reinterpret_cast<v4f*>(dst) = v;
+            } else {
+              for (int x = 0; x < 4 && 4 * part + x < npg; ++x) dst[x] = src[x];
+            }
           }
           __syncthreads();
           jbase = j + 1;
