@@ -1,0 +1,215 @@
+// Decode kernel of the paged MXFP4 index scorer (gfx950).
+#include "mxs_device.h"
+
+namespace mxs {
+namespace {
+using namespace dev;
+
+// ---------------------------------------------------------------------------
+// Decode: one wave per (request, group of 64 heads, chunk of <= 64 pages).
+// Each page is read by exactly one wave, so K goes straight from HBM into
+// registers (staging it in LDS would buy nothing): per 16-token tile, lane
+// (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
+// per wave instruction) and e8m0 byte g of that token. Pages are double-
+// buffered in registers: the loads of page j+2 are in flight while page j+1
+// is scored. The chunk's page ids are read once into one VGPR (lane l holds
+// the id of page j0 + l) and picked per page with readlane.
+// ---------------------------------------------------------------------------
+template <int P>
+struct RegPage {
+  u4 d[P / 16];
+  int s[P / 16];
+};
+
+// One page into registers. dp/sp are the page's (uniform) bases; doff/soff the
+// lane's byte offsets inside the page (data: 64 i + 16 g; scale: 4 i + g).
+template <int P>
+__device__ __forceinline__ void load_reg_page(RegPage<P>& kp, const uint8_t* dp, const uint8_t* sp, uint32_t doff,
+                                              uint32_t soff) {
+#pragma unroll
+  for (int t = 0; t < P / 16; ++t) {
+    kp.d[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 1024u * t));
+    kp.s[t] = __builtin_nontemporal_load(sp + soff + 64u * t);
+  }
+}
+
+// Score one register-resident page against the wave's four query tiles.
+// MASK: the page holds the end of the live window (tokens >= lip are dead).
+// The tile loop is software-pipelined by hand: the four MFMAs of tile t are
+// issued before the results of tile t-1 are folded, and a scheduling fence
+// after each step keeps only two tiles of results live.
+template <int P, bool MASK, bool LG>
+__device__ __forceinline__ void decode_page(const RegPage<P>& kp, const v8i (&qt)[4], int j, int lip, int g,
+                                            const bool (&hv)[4], float* stage, int jrel, float* lg_row,
+                                            const int64_t (&hoff)[4], const KArgs& a) {
+  constexpr int TPP = P / 16;
+  const float s = a.sm_scale;
+  float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  v4f prev[4];
+  const int lrel = lip - 4 * g;   // token 16 tp + 4 g + v is live iff 16 tp + v < lrel
+#pragma unroll
+  for (int t = 0; t <= TPP; ++t) {
+    v4f cur[4];
+    if (t < TPP) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) cur[n] = mma_kq(kp.d[t], qt[n], kp.s[t]);
+    }
+    if (t > 0) {
+      const int tp = t - 1;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        v4f c = prev[n];
+        if constexpr (MASK) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) c[v] = (16 * tp + v < lrel) ? c[v] : kNegInf;
+        }
+        m[n] = max_into(m[n], c);
+        if constexpr (LG) {
+          if (hv[n])
+            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * tp + 4 * g, c * s, a.max_seq_len,
+                          a.vec_lg);
+        }
+      }
+    }
+    if (t < TPP) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) prev[n] = cur[n];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const float r = fold_groups(m[n]);
+    if (g == 0) stage[(16 * n + (threadIdx.x & 15)) * kDecodeStageStride + jrel] = r * s;
+  }
+}
+
+template <int QDT, int P, bool LG>
+__global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
+  constexpr int TPP = P / 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i = lane & 15;
+  // the wave index is uniform across the wave: keep everything derived from it scalar
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
+  if (item >= a.items) return;
+  const int hg = (int)(item % a.head_groups);
+  const int64_t rest = item / a.head_groups;
+  const int pc = (int)(rest % a.page_items);
+  const int b = (int)(rest / a.page_items);
+
+  const int limit = clampi(a.seq[b], 0, a.max_seq_len);
+  const int live_pages = (limit + P - 1) / P;
+  const int j0 = pc * a.pages_per_item;
+  const int j1 = min(j0 + a.pages_per_item, a.NB);
+  const int jl = min(j1, live_pages);                 // pages [j0, jl) are scored
+
+  // the chunk's page ids first (lane l: page j0 + l), so their latency overlaps the query loads
+  const int my_page = (j0 + lane < jl) ? a.bt[(int64_t)b * a.bt_stride + j0 + lane] : 0;
+  v8i qt[4];
+  bool hv[4];
+  int64_t hoff[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int h = hg * kDecodeHeads + n * 16 + i;
+    hv[n] = h < a.H;
+    const int hc = hv[n] ? h : a.H - 1;
+    hoff[n] = (int64_t)hc;
+    qt[n] = load_q_tile_masked<QDT>(a.q + (int64_t)b * a.q_row_stride + (int64_t)hc * a.q_head_stride, g, hv[n]);
+  }
+  float* bs_row = a.bs + (int64_t)b * a.bs_row_stride;
+  float* lg_row = LG ? a.lg + (int64_t)b * a.lg_row_stride : nullptr;
+  // this wave's staging area for its block scores: [64 heads][pages of the chunk]
+  __shared__ float stage_all[kWaves][kDecodeHeads * kDecodeStageStride];
+  float* stage = stage_all[wave];
+
+  if (j0 < jl) {
+    const uint32_t doff = (uint32_t)(i * 64 + 16 * g);
+    const uint32_t soff = (uint32_t)(i * 4 + g);
+    auto load_page = [&](RegPage<P>& kp, int j) {
+      const int jj = min(j, jl - 1);
+      const int64_t page = __builtin_amdgcn_readlane(my_page, jj - j0);
+      load_reg_page<P>(kp, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, doff, soff);
+    };
+    auto score = [&](const RegPage<P>& kp, int j) {
+      const int lip = limit - j * P;                 // live tokens in this page
+      if (lip >= P)
+        decode_page<P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+      else
+        decode_page<P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+    };
+    RegPage<P> A, B;
+    load_page(A, j0);
+    load_page(B, j0 + 1);
+    // the fences stop the scheduler from hoisting a refill above the scoring
+    // of the buffer it overwrites (that would keep three pages live)
+    for (int j = j0; j < jl; j += 2) {
+      score(A, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(A, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < jl) score(B, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(B, j + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // pages past the live window: -inf
+  for (int j = max(j0, jl); j < j1; ++j) {
+    if (g == 0)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) stage[(16 * n + i) * kDecodeStageStride + (j - j0)] = kNegInf;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (hv[n]) {
+        if constexpr (LG) {
+          const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+          for (int t = 0; t < TPP; ++t)
+            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+        }
+      }
+    }
+  }
+  // Block scores leave LDS as one contiguous run of (j1 - j0) floats per head:
+  // consecutive lanes write consecutive pages, so every store instruction
+  // covers whole cache lines instead of 64 scattered 4-byte words.
+  const int npg = j1 - j0;
+  const int nh = min(kDecodeHeads, a.H - hg * kDecodeHeads);
+  for (int idx = lane; idx < nh * npg; idx += 64) {
+    const int h = idx / npg, p = idx - h * npg;
+    bs_row[(int64_t)(hg * kDecodeHeads + h) * a.bs_head_stride + j0 + p] = stage[h * kDecodeStageStride + p];
+  }
+}
+
+template <typename K>
+int occ_of(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), kThreads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int QDT, int P>
+hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<KArgs*>(&a)};
+  const void* fn = a.lg ? reinterpret_cast<const void*>(&k_decode<QDT, P, true>)
+                        : reinterpret_cast<const void*>(&k_decode<QDT, P, false>);
+  return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  if (plan.q_dtype == MXS_Q_BF16)
+    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
+  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+}
+
+int occupancy_decode(int32_t q_dtype, int32_t page_size) {
+  if (q_dtype == MXS_Q_BF16)
+    return page_size == 128 ? occ_of(&k_decode<MXS_Q_BF16, 128, false>) : occ_of(&k_decode<MXS_Q_BF16, 64, false>);
+  return page_size == 128 ? occ_of(&k_decode<MXS_Q_E4M3, 128, false>) : occ_of(&k_decode<MXS_Q_E4M3, 64, false>);
+}
+
+}  // namespace mxs

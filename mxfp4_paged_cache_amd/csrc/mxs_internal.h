@@ -60,10 +60,20 @@ struct KArgs {
   int32_t vec_lg;           // logit rows 16-byte aligned
 };
 
-// Launchers (mxs_kernels.hip). Return the HIP status of the launch.
-hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
+// Launchers (mxs_decode.hip, mxs_prefill.hip). Return the HIP status of the launch.
+hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 
-// Workgroups of `kernel` (for the given q dtype and page size) that fit on one CU.
-int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size);
+// Workgroups of the kernel (for the given q dtype and page size) that fit on one CU.
+int occupancy_decode(int32_t q_dtype, int32_t page_size);
+int occupancy_prefill(int32_t q_dtype, int32_t page_size);
+
+inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  return plan.kernel == KID_DECODE ? launch_decode(plan, a, stream) : launch_prefill(plan, a, stream);
+}
+
+inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size) {
+  return kernel == KID_DECODE ? occupancy_decode(q_dtype, page_size) : occupancy_prefill(q_dtype, page_size);
+}
 
 }  // namespace mxs

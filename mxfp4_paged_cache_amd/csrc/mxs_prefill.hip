@@ -1,0 +1,280 @@
+// Prefill / logits kernel of the paged MXFP4 index scorer (gfx950).
+// Compiled without NaN semantics for float arithmetic (see the build): the
+// kernel only compares and folds finite scores and -inf.
+#include "mxs_device.h"
+
+namespace mxs {
+namespace {
+using namespace dev;
+
+// ---------------------------------------------------------------------------
+// Prefill (also the logits path for now): one workgroup per work item
+// (request, block of 256 query slots, chunk of pages), looping over items
+// with a grid stride. A query slot is (row, head); slot = row * H + head, so
+// a 16-slot tile is 16 heads of one row when H is a multiple of 16. Each wave
+// keeps 4 query tiles in registers for the whole item; every page is staged
+// once per workgroup in LDS (double-buffered, 8.5 KB per buffer at P = 128)
+// and read by all four waves. Block scores are staged in LDS for up to 32
+// pages and leave as contiguous per-slot rows.
+//
+// Work items are ordered page chunk fastest. With a grid and a chunk count
+// that are both multiples of 8, workgroup c only ever sees chunks c mod 8;
+// workgroups are dispatched round-robin over the 8 XCDs, so each XCD reads
+// one eighth of the pages and keeps them in its own L2.
+// ---------------------------------------------------------------------------
+template <int P>
+struct PageStage {
+  static constexpr int kDataChunks = P * 64 / 16 / kThreads;   // 16-byte chunks per thread
+  u4 d[kDataChunks];
+  uint32_t sc;
+};
+
+// LDS layout of a staged page: the data of 16-token tile t is stored as
+// [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
+// a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
+// scales follow as [token][4 bytes] at P * 64. Thread tid fills LDS slot
+// s = tid + 256 c (16 bytes, contiguous writes) with global bytes
+// 16 g..16 g+15 of token 16 t + i, (t, g, i) = (s / 64, s / 16 % 4, s % 16):
+// a wave still loads one contiguous 1 KB tile per instruction.
+template <int P>
+__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
+    const int sl = tid + kThreads * c;
+    const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
+    st.d[c] = *reinterpret_cast<const u4*>(dp + off);
+  }
+  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+}
+
+template <int P>
+__device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
+    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
+  if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
+}
+
+constexpr int kPrefillStagePages = 32;                      // pages per block-score flush
+constexpr int kPrefillStageStride = kPrefillStagePages + 1; // LDS row pitch (odd: no bank conflicts)
+constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;  // query slots per work item
+
+// Score one LDS-resident page against this wave's query tiles; r[n] gets the
+// (unscaled) max over the page's live tokens for slot (tile n, lane i).
+// The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
+// most two tiles of MFMA results are live.
+template <int P, bool MASK, bool LG>
+__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[kPrefillTiles],
+                                             const int (&lrel)[kPrefillTiles], int j, int g, int i,
+                                             float (&r)[kPrefillTiles], float* const (&lrow)[kPrefillTiles],
+                                             const KArgs& a) {
+  constexpr int TPP = P / 16;
+  constexpr int NQ = kPrefillTiles;
+  const uint8_t* kdl = kb + g * 256 + i * 16;     // this lane's 16 bytes of tile t: kdl + 1024 t
+  const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
+  float m[NQ];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
+  auto mma = [&](u4 k, int sc, v4f (&c)[NQ]) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) c[n] = mma_kq(k, qt[n], sc);
+  };
+  auto fold = [&](int t, const v4f (&cc)[NQ]) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      v4f c = cc[n];
+      if constexpr (MASK) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel[n]) ? c[v] : kNegInf;
+      }
+      m[n] = max_into(m[n], c);
+      if constexpr (LG) {
+        if (lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * a.sm_scale, a.max_seq_len, a.vec_lg);
+      }
+    }
+  };
+  // two tiles per trip, no MFMA result carried across trips; the next pair of
+  // K tiles is read from LDS while this pair is multiplied and folded
+  u4 k0 = *reinterpret_cast<const u4*>(kdl);
+  int s0 = ksl[0];
+  u4 k1 = *reinterpret_cast<const u4*>(kdl + 1024);
+  int s1 = ksl[64];
+#pragma unroll 1
+  for (int t = 0; t < TPP; t += 2) {
+    v4f cA[NQ], cB[NQ];
+    mma(k0, s0, cA);
+    mma(k1, s1, cB);
+    if (t + 2 < TPP) {
+      k0 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 2));
+      s0 = ksl[64 * (t + 2)];
+      k1 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 3));
+      s1 = ksl[64 * (t + 3)];
+    }
+    fold(t, cA);
+    fold(t + 1, cB);
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
+}
+
+template <int QDT, int P, bool WANT_BS, bool WANT_LG>
+__global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
+  constexpr int NQ = kPrefillTiles;
+  constexpr int PB = P * 68;   // bytes of one staged page
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
+  __shared__ float stage[WANT_BS ? kPrefillSlots * kPrefillStageStride : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const float s = a.sm_scale;
+  const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
+
+  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int pc = (int)(item % a.page_items);
+    const int64_t rest = item / a.page_items;
+    const int sb = (int)(rest % a.slot_items);
+    const int b = (int)(rest / a.slot_items);
+    const int row0 = a.cu[b];
+    const int qlen = a.cu[b + 1] - row0;
+    const int64_t nslots = (int64_t)qlen * a.H;
+    const int64_t sbeg = (int64_t)sb * kPrefillSlots;
+    if (sbeg >= nslots) continue;   // uniform over the workgroup
+    const int seq = a.seq[b], pre = a.prefix[b];
+    const int64_t slast = min(sbeg + (int64_t)kPrefillSlots, nslots) - 1;
+    const int item_lim = clampi(min(seq, pre + (int)(slast / a.H) + 1), 0, a.max_seq_len);
+
+    // this lane's query slots
+    v8i qt[NQ];
+    int lim[NQ];
+    float* lrow[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int64_t sl = sbeg + (int64_t)(wave * NQ + n) * 16 + i;
+      const bool valid = sl < nslots;
+      const int64_t slc = valid ? sl : nslots - 1;
+      const int r = (int)(slc / a.H);
+      const int h = (int)(slc % a.H);
+      const int64_t grow = (int64_t)row0 + r;
+      lim[n] = valid ? clampi(min(seq, pre + r + 1), 0, a.max_seq_len) : 0;
+      qt[n] = load_q_tile_masked<QDT>(a.q + grow * a.q_row_stride + (int64_t)h * a.q_head_stride, g, valid);
+      lrow[n] = (WANT_LG && valid) ? a.lg + grow * a.lg_row_stride + (int64_t)h * a.lg_head_stride : nullptr;
+    }
+    // smallest limit among this wave's slots: the limit of its first slot
+    const int64_t wfirst = sbeg + (int64_t)wave * NQ * 16;
+    const int wave_min_lim = wfirst < nslots ? clampi(min(seq, pre + (int)(wfirst / a.H) + 1), 0, a.max_seq_len) : 0;
+
+    const int j0 = pc * a.pages_per_item;
+    const int j1 = min(j0 + a.pages_per_item, a.NB);
+    const int jl = min(j1, (item_lim + P - 1) / P);   // pages [j0, jl) hold live tokens
+    const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+
+    if (j0 < jl) {
+      PageStage<P> st;
+      const int64_t page = btrow[j0];
+      stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+      stage_store<P>(st, kbuf, tid);
+    }
+    __syncthreads();
+    int jbase = j0;
+    for (int j = j0; j < j1; ++j) {
+      float r[NQ];
+      if (j < jl) {
+        const bool more = j + 1 < jl;
+        PageStage<P> nx;
+        if (more) {
+          const int64_t page = btrow[j + 1];
+          stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+        }
+        const uint8_t* kb = kbuf + ((j - j0) & 1) * PB;
+        int lrel[NQ];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) lrel[n] = lim[n] - j * P - 4 * g;
+        if ((j + 1) * P > wave_min_lim)
+          prefill_page<P, true, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+        else
+          prefill_page<P, false, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+        if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
+      } else {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) r[n] = kNegInf;
+        if constexpr (WANT_LG) {
+#pragma unroll
+          for (int n = 0; n < NQ; ++n)
+            if (lrow[n])
+#pragma unroll
+              for (int t = 0; t < P / 16; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
+        }
+      }
+      if constexpr (WANT_BS) {
+        if (g == 0) {
+#pragma unroll
+          for (int n = 0; n < NQ; ++n) stage[((wave * NQ + n) * 16 + i) * kPrefillStageStride + (j - jbase)] = r[n] * s;
+        }
+      }
+      __syncthreads();
+      if constexpr (WANT_BS) {
+        if (j - jbase == kPrefillStagePages - 1 || j == j1 - 1) {
+          // flush pages [jbase, j]: 8 threads per slot row, 4 pages per thread,
+          // so each group of 8 threads writes one contiguous run of the row
+          const int npg = j - jbase + 1;
+          const int nvalid = (int)min((int64_t)kPrefillSlots, nslots - sbeg);
+          const int part = tid & 7;
+          const bool vec = a.vec_bs && (jbase & 3) == 0 && 4 * part + 3 < npg;
+          for (int sl = tid >> 3; sl < nvalid; sl += kThreads / 8) {
+            if (4 * part >= npg) continue;
+            const uint32_t slot = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H)) + (uint32_t)sl;  // slot - H * row(sbeg)
+            const uint32_t dr = slot / (uint32_t)a.H;
+            const int64_t grow = (int64_t)row0 + sbeg / a.H + dr;
+            float* dst = a.bs + grow * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride + jbase +
+                         4 * part;
+            const float* src = stage + sl * kPrefillStageStride + 4 * part;
+            if (vec) {
+              const v4f v = {src[0], src[1], src[2], src[3]};
+              *reinterpret_cast<v4f*>(dst) = v;
+            } else {
+              for (int x = 0; x < 4 && 4 * part + x < npg; ++x) dst[x] = src[x];
+            }
+          }
+          __syncthreads();
+          jbase = j + 1;
+        }
+      }
+    }
+  }
+}
+
+template <typename K>
+int occ_of(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), kThreads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int QDT, int P>
+hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<KArgs*>(&a)};
+  const bool bs = a.bs != nullptr, lg = a.lg != nullptr;
+  const void* fn = bs && lg ? reinterpret_cast<const void*>(&k_prefill<QDT, P, true, true>)
+                   : bs     ? reinterpret_cast<const void*>(&k_prefill<QDT, P, true, false>)
+                            : reinterpret_cast<const void*>(&k_prefill<QDT, P, false, true>);
+  return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+  if (plan.q_dtype == MXS_Q_BF16)
+    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
+  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+}
+
+int occupancy_prefill(int32_t q_dtype, int32_t page_size) {
+  if (q_dtype == MXS_Q_BF16)
+    return page_size == 128 ? occ_of(&k_prefill<MXS_Q_BF16, 128, true, false>)
+                            : occ_of(&k_prefill<MXS_Q_BF16, 64, true, false>);
+  return page_size == 128 ? occ_of(&k_prefill<MXS_Q_E4M3, 128, true, false>)
+                          : occ_of(&k_prefill<MXS_Q_E4M3, 64, true, false>);
+}
+
+}  // namespace mxs
