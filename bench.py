@@ -13,6 +13,18 @@ triples per second; the line also carries us/call, achieved HBM GB/s and
 scaled-MFMA utilisation, the roofline of the dominant kernel and the CPU
 oracle's rate on a bounded sample of the same workload.
 
+The K timed steps are captured once in a HIP graph and replayed, so the
+host's launch overhead is not part of the time; HIP events on the replay
+stream bracket the replay. Each step is one kernel launch, so the per-step
+time is the kernel's average launch duration (--eager times plain launches).
+
+HBM traffic: `--copy-probe` adds a plain 1 GiB float32 negation (reads and
+writes 2^30 bytes) ahead of the warmup, so that one `rocprofv3 --pmc
+FETCH_SIZE` run and one `--pmc WRITE_SIZE` run see the scorer and a kernel
+of known size; `--pmc-summary DB...` turns the two runs' databases into a
+traffic file (counter readings scaled by known bytes / copy reading), which
+the roofline picks up while the kernel sources still hash the same.
+
 --config selects another workload (1: prefill 64 rows ctx 1k with logits,
 3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
 5: logits, 64-token pages in a shared pool past 4.608e9 bytes).
@@ -20,6 +32,8 @@ oracle's rate on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,8 +48,64 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0     # dense fp8 rate; the fp4 x fp8 scaled MFMA is
 MFMA_FP4_PEAK_TFLOPS = 10100.0    # dense fp4 x fp4, for reference
 
 
+COPY_PROBE_BYTES = 1 << 30        # bytes read (and written) by the --copy-probe kernel
+PROFILES = os.path.join(ROOT, "profiles")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_name(mode: str) -> str:
+    return "k_decode" if mode == "decode" else "k_prefill"
+
+
+def kernel_source_hash() -> str:
+    """Hash of everything that determines the kernels' machine code."""
+    pkg = os.path.join(ROOT, "mxfp4_paged_cache_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py"),
+                                                                 os.path.join(ROOT, "include", "mxscore.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(mode: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel_name(mode)}_{workload}_traffic.json")
+
+
+def pmc_summary(dbs):
+    """Per-dispatch averages of FETCH_SIZE / WRITE_SIZE (KiB) for the scorer and
+    the copy probe, from rocprofv3 databases; returns the traffic record."""
+    import sqlite3
+    acc = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        per = {}
+        for name, disp, val, kname in con.execute(
+                "select counter_name, dispatch_id, value, kernel_name from counters_collection"):
+            kind = "copy" if "neg" in kname else ("k_decode" if "k_decode" in kname else
+                                                  ("k_prefill" if "k_prefill" in kname else None))
+            if kind is None:
+                continue
+            per.setdefault((name, kind), {}).setdefault(disp, 0.0)
+            per[(name, kind)][disp] += val
+        for key, d in per.items():
+            acc[key] = sum(d.values()) / len(d)
+    out = {}
+    for counter, field in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        copy = acc.get((counter, "copy"))
+        for k in ("k_decode", "k_prefill"):
+            v = acc.get((counter, k))
+            if v is None or not copy:
+                continue
+            factor = COPY_PROBE_BYTES / (copy * 1024.0)
+            out.setdefault(k, {})[field] = {"counter_kib_per_dispatch": v, "copy_probe_kib": copy,
+                                            "scale": factor, "bytes": v * 1024.0 * factor}
+    return out
 
 
 def algorithmic_bytes(wl, inp) -> int:
@@ -65,8 +135,23 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="rows the oracle scores for the CPU baseline")
-    ap.add_argument("--traffic", type=str, default="", help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--traffic", type=str, default="", help="traffic file (default: the one under profiles/)")
+    ap.add_argument("--eager", action="store_true", help="time plain launches instead of a graph replay")
+    ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB copy kernel first (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="DB",
+                    help="summarize rocprofv3 --pmc databases into a traffic record and exit")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        from mxfp4_paged_cache_amd import workloads as W
+        wl = W.CONFIGS[args.config]()
+        rec = pmc_summary(args.pmc_summary).get(kernel_name(wl.mode), {})
+        rec = {"workload": wl.name, "kernel": kernel_name(wl.mode), "source_hash": kernel_source_hash(),
+               "copy_probe_bytes": COPY_PROBE_BYTES, **rec}
+        if "read" in rec and "write" in rec:
+            rec["bytes_per_launch"] = rec["read"]["bytes"] + rec["write"]["bytes"]
+        print(json.dumps(rec, indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the scorer needs no "
@@ -116,17 +201,42 @@ def main():
             mx.score_prefill(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
                              max(wl.q_lens), Wd, S, out=bs, logits=lg if lg is not None else False, plan=plan)
 
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
+    graph = None
+    if not args.eager:
+        # capture the K timed steps once (side stream warm-up first, as capture requires)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            call(0)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                call(i)
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)   # the launches (or the replay) run on this stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        call(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            call(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -141,10 +251,12 @@ def main():
     tflops = flops / (ms / 1e3) / 1e12
     hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64)
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    tpath = args.traffic or traffic_path(wl.mode, wl.name)
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("workload") == wl.name:
+        # counters taken on other kernel code no longer describe this kernel
+        if tr.get("workload") == wl.name and tr.get("source_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -183,6 +295,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
+        "timing": "eager launches" if graph is None else "graph replay of the timed steps",
+        "kernel": kernel_name(wl.mode),
     }
     print(json.dumps(line), flush=True)
 
