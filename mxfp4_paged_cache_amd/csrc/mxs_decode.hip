@@ -6,7 +6,7 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
-// Decode: one wave per (request, group of 64 heads, chunk of <= 64 pages).
+// Decode: one wave per (request, group of 64 heads, chunk of <= 32 pages).
 // Each page is read by exactly one wave, so K goes straight from HBM into
 // registers (staging it in LDS would buy nothing): per 16-token tile, lane
 // (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
