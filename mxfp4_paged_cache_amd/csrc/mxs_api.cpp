@@ -152,7 +152,9 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     if (chunks < ceil_div(NB, mxs::kDecodeMaxPages)) chunks = ceil_div(NB, mxs::kDecodeMaxPages);
     if (chunks < 1) chunks = 1;
     p.pages_per_item = (int32_t)(NB > 0 ? ceil_div(NB, chunks) : 1);
-    p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, p.pages_per_item) : 1);
+    // a multiple of 4 chunks, so the 4 waves of a workgroup share (request,
+    // head group) and can share its query tiles; surplus chunks are empty
+    p.page_items = (int32_t)(ceil_div(NB > 0 ? ceil_div(NB, p.pages_per_item) : 1, mxs::kWaves) * mxs::kWaves);
     p.slot_items = 1;
     p.slots_per_item = num_heads;
     p.items = lanes * p.page_items;
@@ -226,6 +228,23 @@ int check_out(const char* name, const mxs_out* o, int64_t rows, int32_t H, int64
   if (!mul_add(rows - 1, o->row_stride, row_span, &span) || span > INT64_MAX / 4)
     return fail(MXS_ELAYOUT, "%s output span overflows", name);
   return MXS_OK;
+}
+
+// The structural invariants the kernels rely on (a caller may pass a plan
+// it has modified or made for another device).
+bool plan_consistent(const mxs_plan& p, int mode, int32_t H, int32_t B, int32_t max_query_len, int64_t NB) {
+  if (p.block != mxs::kThreads || p.grid < 1 || p.pages_per_item < 1 || p.page_items < 1) return false;
+  if ((int64_t)p.page_items * p.pages_per_item < NB) return false;
+  if (mode == MXS_MODE_DECODE) {
+    return p.kernel == mxs::KID_DECODE && p.head_groups == ceil_div(H, mxs::kDecodeHeads) &&
+           p.pages_per_item <= mxs::kDecodeMaxPages && p.page_items % mxs::kWaves == 0 &&
+           p.items == (int64_t)B * p.head_groups * p.page_items && (int64_t)p.grid * mxs::kWaves == p.items;
+  }
+  const int32_t kid = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+  const int64_t slots = (int64_t)max_query_len * H;
+  return p.kernel == kid && p.slots_per_item == mxs::kWaves * mxs::kPrefillTiles * 16 &&
+         p.slot_items == (slots > 0 ? ceil_div(slots, p.slots_per_item) : 0) &&
+         p.items == (int64_t)B * p.slot_items * p.page_items && p.grid <= (p.items > 0 ? p.items : 1);
 }
 
 int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt, float sm_scale,
@@ -315,6 +334,8 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
                        want_bs, 0, &plan);
     if (rc != MXS_OK) return rc;
   }
+  if (!plan_consistent(plan, mode, H, bt->batch, decode ? 1 : bt->max_query_len, NB))
+    return fail(MXS_EINVAL, "the plan's work decomposition is inconsistent with its shapes");
   if (plan.items == 0) return MXS_OK;
 
   mxs::KArgs a;

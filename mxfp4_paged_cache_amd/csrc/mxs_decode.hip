@@ -14,6 +14,14 @@ using namespace dev;
 // buffered in registers: the loads of page j+2 are in flight while page j+1
 // is scored. The chunk's page ids are read once into one VGPR (lane l holds
 // the id of page j0 + l) and picked per page with readlane.
+//
+// Wave items are ordered page chunk fastest, and the plan makes the chunk
+// count a multiple of 4, so the four waves of a workgroup share (request,
+// head group): they load the query tiles once, one tile each, and exchange
+// them through LDS. Workgroups are dispatched round-robin over the 8 XCDs;
+// renumbering them so that each XCD gets a contiguous range of workgroups
+// keeps all chunks of a request on one XCD, whose L2 then serves the
+// request's query and block-table row to every chunk.
 // ---------------------------------------------------------------------------
 template <int P>
 struct RegPage {
@@ -91,21 +99,36 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   const int g = lane >> 4, i = lane & 15;
   // the wave index is uniform across the wave: keep everything derived from it scalar
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-  if (item >= a.items) return;
-  const int hg = (int)(item % a.head_groups);
-  const int64_t rest = item / a.head_groups;
-  const int pc = (int)(rest % a.page_items);
-  const int b = (int)(rest / a.page_items);
+  int blk = blockIdx.x;
+  if ((gridDim.x & 7) == 0) blk = (blk & 7) * (int)(gridDim.x >> 3) + (blk >> 3);
+  // the plan launches exactly items / 4 workgroups; the guard only keeps a
+  // stray wave harmless (it still takes part in the barrier below)
+  const bool active = (int64_t)blk * kWaves + wave < a.items;
+  const int64_t item = active ? (int64_t)blk * kWaves + wave : (int64_t)blk * kWaves;
+  const int pc = (int)(item % a.page_items);
+  const int64_t rest = item / a.page_items;
+  const int hg = (int)(rest % a.head_groups);
+  const int b = (int)(rest / a.head_groups);
 
   const int limit = clampi(a.seq[b], 0, a.max_seq_len);
   const int live_pages = (limit + P - 1) / P;
   const int j0 = pc * a.pages_per_item;
-  const int j1 = min(j0 + a.pages_per_item, a.NB);
+  const int j1 = max(j0, min(j0 + a.pages_per_item, a.NB));   // chunks past NB are empty
   const int jl = min(j1, live_pages);                 // pages [j0, jl) are scored
 
   // the chunk's page ids first (lane l: page j0 + l), so their latency overlaps the query loads
-  const int my_page = (j0 + lane < jl) ? a.bt[(int64_t)b * a.bt_stride + j0 + lane] : 0;
+  const int my_page = (active && j0 + lane < jl) ? a.bt[(int64_t)b * a.bt_stride + j0 + lane] : 0;
+  // query tile `wave` of the workgroup's 64 heads, rounded to e4m3, shared through LDS
+  __shared__ v8i q_share[kWaves][64];
+  {
+    const int h = hg * kDecodeHeads + wave * 16 + i;
+    const bool v = h < a.H;
+    const int hc = v ? h : a.H - 1;
+    q_share[wave][lane] =
+        load_q_tile_masked<QDT>(a.q + (int64_t)b * a.q_row_stride + (int64_t)hc * a.q_head_stride, g, v);
+  }
+  __syncthreads();
+  if (!active) return;
   v8i qt[4];
   bool hv[4];
   int64_t hoff[4];
@@ -113,9 +136,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   for (int n = 0; n < 4; ++n) {
     const int h = hg * kDecodeHeads + n * 16 + i;
     hv[n] = h < a.H;
-    const int hc = hv[n] ? h : a.H - 1;
-    hoff[n] = (int64_t)hc;
-    qt[n] = load_q_tile_masked<QDT>(a.q + (int64_t)b * a.q_row_stride + (int64_t)hc * a.q_head_stride, g, hv[n]);
+    hoff[n] = (int64_t)(hv[n] ? h : a.H - 1);
+    qt[n] = q_share[n][lane];
   }
   float* bs_row = a.bs + (int64_t)b * a.bs_row_stride;
   float* lg_row = LG ? a.lg + (int64_t)b * a.lg_row_stride : nullptr;

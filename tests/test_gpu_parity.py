@@ -257,6 +257,21 @@ def test_rejections_on_gpu_tensors():
     pl = torch.tensor([0, 0], dtype=torch.int32, device=dev)
     with pytest.raises(ValueError):
         mx.score_prefill(q, kd, ks, bt, cu, sl, pl, 1, 256, S, out=torch.empty((2, 4, 3), device=dev))
+    # plans whose work decomposition was altered after planning are refused before launch
+    pd = mx.make_plan("decode", torch.bfloat16, 128, 4, 2, 1, 256, False, True)
+    assert mx.score_decode(q, kd, ks, bt, sl, 256, S, plan=pd).shape == (2, 4, 2)
+    for field, val in (("pages_per_item", 64), ("grid", pd.grid + 1), ("page_items", pd.page_items + 1),
+                       ("head_groups", 2)):
+        bad = type(pd).from_buffer_copy(bytes(pd))
+        setattr(bad, field, val)
+        with pytest.raises(ValueError):
+            mx.score_decode(q, kd, ks, bt, sl, 256, S, plan=bad)
+    pp = mx.make_plan("prefill", torch.bfloat16, 128, 4, 2, 1, 256, False, True)
+    for field, val in (("slots_per_item", 128), ("items", pp.items + 1), ("pages_per_item", 0)):
+        bad = type(pp).from_buffer_copy(bytes(pp))
+        setattr(bad, field, val)
+        with pytest.raises(ValueError):
+            mx.score_prefill(q, kd, ks, bt, cu, sl, pl, 1, 256, S, plan=bad)
 
 
 # ------------------------------------------------------------------ full-size workloads (sampled oracle)
