@@ -17,10 +17,15 @@ using namespace dev;
 // and read by all four waves. Block scores are staged in LDS for up to 32
 // pages and leave as contiguous per-slot rows.
 //
-// Work items are ordered page chunk fastest. With a grid and a chunk count
-// that are both multiples of 8, workgroup c only ever sees chunks c mod 8;
-// workgroups are dispatched round-robin over the 8 XCDs, so each XCD reads
-// one eighth of the pages and keeps them in its own L2.
+// Block-score work items are ordered slot block fastest: at any moment the
+// whole grid works on one chunk of pages (small enough for every XCD's L2),
+// and each workgroup's items are spread over all query rows and all chunks,
+// so the causal triangle (chunks past some rows' limits are cheap) costs
+// every workgroup the same. When logits are written, items are ordered page
+// chunk fastest instead: with a grid and a chunk count that are both
+// multiples of 8, workgroup c only sees chunks c mod 8 (workgroups go
+// round-robin over the 8 XCDs), so each XCD keeps one eighth of the pages in
+// its own L2.
 // ---------------------------------------------------------------------------
 template <int P>
 struct PageStage {
@@ -130,10 +135,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
   const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
 
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
-    const int pc = (int)(item % a.page_items);
-    const int64_t rest = item / a.page_items;
-    const int sb = (int)(rest % a.slot_items);
-    const int b = (int)(rest / a.slot_items);
+    int pc, sb, b;
+    if constexpr (WANT_LG) {
+      pc = (int)(item % a.page_items);
+      const int64_t rest = item / a.page_items;
+      sb = (int)(rest % a.slot_items);
+      b = (int)(rest / a.slot_items);
+    } else {
+      sb = (int)(item % a.slot_items);
+      const int64_t rest = item / a.slot_items;
+      pc = (int)(rest % a.page_items);
+      b = (int)(rest / a.page_items);
+    }
     const int row0 = a.cu[b];
     const int qlen = a.cu[b + 1] - row0;
     const int64_t nslots = (int64_t)qlen * a.H;
@@ -168,9 +181,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     const int jl = min(j1, (item_lim + P - 1) / P);   // pages [j0, jl) hold live tokens
     const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
 
+    // page ids, 64 at a time: lane l holds the id of page jid + l (one table
+    // read per 64 pages, picked per page with readlane, so no page waits on
+    // a table read before its loads can issue)
+    int jid = j0;
+    int ids = (j0 + lane < jl) ? btrow[j0 + lane] : 0;
     if (j0 < jl) {
       PageStage<P> st;
-      const int64_t page = btrow[j0];
+      const int64_t page = __builtin_amdgcn_readfirstlane(ids);
       stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
       stage_store<P>(st, kbuf, tid);
     }
@@ -182,7 +200,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
         const bool more = j + 1 < jl;
         PageStage<P> nx;
         if (more) {
-          const int64_t page = btrow[j + 1];
+          if (j + 1 - jid == 64) {
+            jid += 64;
+            ids = (jid + lane < jl) ? btrow[jid + lane] : 0;
+          }
+          const int64_t page = __builtin_amdgcn_readlane(ids, j + 1 - jid);
           stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
         }
         const uint8_t* kb = kbuf + ((j - j0) & 1) * PB;
