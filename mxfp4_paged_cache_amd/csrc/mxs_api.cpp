@@ -78,15 +78,15 @@ int current_device(int* dev, DeviceInfo* info) {
   return MXS_OK;
 }
 
-int occupancy_cached(int dev, int32_t kernel, int32_t q_dtype, int32_t page_size) {
+int occupancy_cached(int dev, int32_t kernel, int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
   const uint64_t key = ((uint64_t)(uint32_t)dev << 32) | ((uint64_t)kernel << 16) | ((uint64_t)q_dtype << 8) |
-                       (uint64_t)(page_size == 128 ? 1 : 0);
+                       (uint64_t)(page_size == 128 ? 1 : 0) | (want_bs ? 2u : 0u) | (want_lg ? 4u : 0u);
   {
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_occupancy.find(key);
     if (it != g_occupancy.end()) return it->second;
   }
-  const int occ = mxs::occupancy(kernel, q_dtype, page_size);
+  const int occ = mxs::occupancy(kernel, q_dtype, page_size, want_bs, want_lg);
   std::lock_guard<std::mutex> lock(g_mu);
   g_occupancy[key] = occ;
   return occ;
@@ -164,25 +164,50 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     // items for a few per resident workgroup; the grid loops over them.
     p.kernel = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
     p.head_groups = 1;
-    p.slots_per_item = mxs::kWaves * mxs::kPrefillTiles * 16;
+    p.slots_per_item = mxs::prefill_slots(want_logits != 0);
     const int64_t slots = (int64_t)p.max_query_len * num_heads;
     p.slot_items = (int32_t)(slots > 0 ? ceil_div(slots, p.slots_per_item) : 0);
     const int64_t base = (int64_t)batch * p.slot_items;
-    const int64_t want_items = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * 4 : capacity * 4;
-    int64_t chunks = base > 0 ? ceil_div(want_items, base) : 1;
-    // Page chunks in multiples of 8 (when there are pages enough): with a grid
-    // that is also a multiple of 8, workgroup c only sees chunks c mod 8, so
-    // each of the 8 XCDs reads one eighth of the pages into its own L2.
-    if (NB >= 8) chunks = ceil_div(chunks, 8) * 8;
-    if (chunks > NB) chunks = NB;
-    if (chunks < 1) chunks = 1;
-    int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
-    if (ppi > 4) ppi = ceil_div(ppi, 4) * 4;   // chunk starts stay 16-byte aligned in the score rows
+    int64_t grid = parallel_unit_num > 0 ? parallel_unit_num : capacity;
+    if (parallel_unit_num <= 0 && grid >= 8) grid = grid / 8 * 8;
+    // pages per chunk for a chunk count (chunk starts stay 16-byte aligned in the score rows)
+    auto ppi_for = [&](int64_t chunks) {
+      int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
+      if (ppi > 4) ppi = ceil_div(ppi, 4) * 4;
+      return ppi;
+    };
+    int64_t ppi;
+    if (mode == MXS_MODE_PREFILL && !want_logits) {
+      // Block scores only: the grid strides over items ordered slot block
+      // fastest. Pick the chunk count whose items spread most evenly over the
+      // grid: the work is base * NB page-units, and the busiest workgroup
+      // does ceil(items / grid) items of at most ppi pages each.
+      ppi = ppi_for(1);
+      double best = -1.0;
+      for (int64_t chunks = 1; chunks <= (NB < 64 ? NB : 64); ++chunks) {
+        const int64_t cp = ppi_for(chunks);
+        const int64_t items = base * ceil_div(NB, cp);
+        const double eff = (double)base * (double)NB / ((double)grid * (double)ceil_div(items, grid) * (double)cp);
+        if (eff > best + 0.005) {
+          best = eff;
+          ppi = cp;
+        }
+      }
+    } else {
+      // Logits are written page chunk fastest. Chunk counts in multiples of 8
+      // (when there are pages enough): with a grid that is also a multiple of
+      // 8, workgroup c only sees chunks c mod 8, so each of the 8 XCDs reads
+      // one eighth of the pages into its own L2.
+      const int64_t want_items = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * 4 : capacity * 4;
+      int64_t chunks = base > 0 ? ceil_div(want_items, base) : 1;
+      if (NB >= 8) chunks = ceil_div(chunks, 8) * 8;
+      if (chunks > NB) chunks = NB;
+      if (chunks < 1) chunks = 1;
+      ppi = ppi_for(chunks);
+    }
     p.pages_per_item = (int32_t)ppi;
     p.page_items = (int32_t)(NB > 0 ? ceil_div(NB, ppi) : 1);
     p.items = base * p.page_items;
-    int64_t grid = parallel_unit_num > 0 ? parallel_unit_num : capacity;
-    if (parallel_unit_num <= 0 && grid >= 8) grid = grid / 8 * 8;
     if (grid > p.items) grid = p.items;
     if (grid < 1) grid = 1;
     p.grid = (int32_t)grid;
@@ -203,7 +228,7 @@ int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_
     return fail(MXS_EDTYPE, "query dtype must be bf16 or e4m3; got %d", q_dtype);
   if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
   const int32_t kid = mode == MXS_MODE_DECODE ? mxs::KID_DECODE : mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
-  const int occ = occupancy_cached(dev, kid, q_dtype, page_size);
+  const int occ = occupancy_cached(dev, kid, q_dtype, page_size, want_blocks != 0, want_logits != 0);
   return mxs_plan_make_for(mode, q_dtype, page_size, num_heads, batch, max_query_len, max_seq_len, want_logits,
                            want_blocks, parallel_unit_num, info.cus, occ, plan);
 }
@@ -242,7 +267,7 @@ bool plan_consistent(const mxs_plan& p, int mode, int32_t H, int32_t B, int32_t 
   }
   const int32_t kid = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
   const int64_t slots = (int64_t)max_query_len * H;
-  return p.kernel == kid && p.slots_per_item == mxs::kWaves * mxs::kPrefillTiles * 16 &&
+  return p.kernel == kid && p.slots_per_item == mxs::prefill_slots(p.want_logits != 0) &&
          p.slot_items == (slots > 0 ? ceil_div(slots, p.slots_per_item) : 0) &&
          p.items == (int64_t)B * p.slot_items * p.page_items && p.grid <= (p.items > 0 ? p.items : 1);
 }

@@ -228,10 +228,15 @@ hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t strea
   return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
 }
 
-int occupancy_decode(int32_t q_dtype, int32_t page_size) {
+template <int QDT, int P>
+int occ_qp(bool lg) {
+  return lg ? occ_of(&k_decode<QDT, P, true>) : occ_of(&k_decode<QDT, P, false>);
+}
+
+int occupancy_decode(int32_t q_dtype, int32_t page_size, bool want_lg) {
   if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_of(&k_decode<MXS_Q_BF16, 128, false>) : occ_of(&k_decode<MXS_Q_BF16, 64, false>);
-  return page_size == 128 ? occ_of(&k_decode<MXS_Q_E4M3, 128, false>) : occ_of(&k_decode<MXS_Q_E4M3, 64, false>);
+    return page_size == 128 ? occ_qp<MXS_Q_BF16, 128>(want_lg) : occ_qp<MXS_Q_BF16, 64>(want_lg);
+  return page_size == 128 ? occ_qp<MXS_Q_E4M3, 128>(want_lg) : occ_qp<MXS_Q_E4M3, 64>(want_lg);
 }
 
 }  // namespace mxs

@@ -18,11 +18,16 @@ enum KernelId : int32_t {
 
 constexpr int kWaves = 4;           // waves per workgroup, every kernel
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPrefillTiles = 4;    // 16-slot query tiles per wave (prefill)
+constexpr int kPrefillTiles = 8;    // 16-slot query tiles per wave (prefill, block scores only)
+constexpr int kPrefillTilesLG = 4;  // 16-slot query tiles per wave (prefill writing logits)
 constexpr int kLogitsTiles = 4;     // 16-slot query tiles per wave (logits)
 constexpr int kDecodeHeads = 64;    // heads per decode wave (4 tiles of 16)
 constexpr int kDecodeMaxPages = 32; // pages per decode wave (ids fit one VGPR; scores staged in LDS)
 constexpr int kDecodeStageStride = kDecodeMaxPages + 1;   // LDS row pitch in floats (odd: no bank conflicts)
+
+// Query slots per prefill work item: fewer when logits are written (those
+// variants need more registers for the logit row pointers).
+constexpr int prefill_slots(bool want_logits) { return kWaves * (want_logits ? kPrefillTilesLG : kPrefillTiles) * 16; }
 
 // Everything a kernel needs, by value. Byte strides for query and cache,
 // element strides for int32 tables and fp32 outputs.
@@ -64,16 +69,17 @@ struct KArgs {
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 
-// Workgroups of the kernel (for the given q dtype and page size) that fit on one CU.
-int occupancy_decode(int32_t q_dtype, int32_t page_size);
-int occupancy_prefill(int32_t q_dtype, int32_t page_size);
+// Workgroups of the kernel variant (q dtype, page size, outputs) that fit on one CU.
+int occupancy_decode(int32_t q_dtype, int32_t page_size, bool want_lg);
+int occupancy_prefill(int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg);
 
 inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
   return plan.kernel == KID_DECODE ? launch_decode(plan, a, stream) : launch_prefill(plan, a, stream);
 }
 
-inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size) {
-  return kernel == KID_DECODE ? occupancy_decode(q_dtype, page_size) : occupancy_prefill(q_dtype, page_size);
+inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
+  return kernel == KID_DECODE ? occupancy_decode(q_dtype, page_size, want_lg)
+                              : occupancy_prefill(q_dtype, page_size, want_bs, want_lg);
 }
 
 }  // namespace mxs

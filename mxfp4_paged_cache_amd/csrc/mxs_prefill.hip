@@ -60,21 +60,27 @@ __device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf
   if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
 }
 
-constexpr int kPrefillStagePages = 32;                      // pages per block-score flush
-constexpr int kPrefillStageStride = kPrefillStagePages + 1; // LDS row pitch (odd: no bank conflicts)
-constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;  // query slots per work item
+// Per-variant shape: query tiles per wave, slots per item, and the block-score
+// staging (pages per flush; LDS row pitch odd, so no bank conflicts). With 8
+// tiles a flush window is 16 pages, which keeps two workgroups per CU in LDS.
+template <bool WANT_LG>
+struct PrefillShape {
+  static constexpr int NQ = WANT_LG ? kPrefillTilesLG : kPrefillTiles;
+  static constexpr int kSlots = kWaves * NQ * 16;
+  static constexpr int kStagePages = WANT_LG ? 32 : 16;
+  static constexpr int kStageStride = kStagePages + 1;
+  static constexpr int kFlushThreadsPerRow = kStagePages / 4;   // 4 pages per thread
+};
 
 // Score one LDS-resident page against this wave's query tiles; r[n] gets the
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
 // The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
 // most two tiles of MFMA results are live.
-template <int P, bool MASK, bool LG>
-__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[kPrefillTiles],
-                                             const int (&lrel)[kPrefillTiles], int j, int g, int i,
-                                             float (&r)[kPrefillTiles], float* const (&lrow)[kPrefillTiles],
+template <int P, int NQ, bool MASK, bool LG>
+__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[NQ], const int (&lrel)[NQ], int j,
+                                             int g, int i, float (&r)[NQ], float* const (&lrow)[NQ],
                                              const KArgs& a) {
   constexpr int TPP = P / 16;
-  constexpr int NQ = kPrefillTiles;
   const uint8_t* kdl = kb + g * 256 + i * 16;     // this lane's 16 bytes of tile t: kdl + 1024 t
   const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
   float m[NQ];
@@ -124,7 +130,11 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
 
 template <int QDT, int P, bool WANT_BS, bool WANT_LG>
 __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
-  constexpr int NQ = kPrefillTiles;
+  using S = PrefillShape<WANT_LG>;
+  constexpr int NQ = S::NQ;
+  constexpr int kPrefillSlots = S::kSlots;
+  constexpr int kPrefillStagePages = S::kStagePages;
+  constexpr int kPrefillStageStride = S::kStageStride;
   constexpr int PB = P * 68;   // bytes of one staged page
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
   __shared__ float stage[WANT_BS ? kPrefillSlots * kPrefillStageStride : 1];
@@ -212,9 +222,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) lrel[n] = lim[n] - j * P - 4 * g;
         if ((j + 1) * P > wave_min_lim)
-          prefill_page<P, true, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+          prefill_page<P, NQ, true, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
         else
-          prefill_page<P, false, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+          prefill_page<P, NQ, false, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
         if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
       } else {
 #pragma unroll
@@ -235,14 +245,17 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       }
       __syncthreads();
       if constexpr (WANT_BS) {
-        if (j - jbase == kPrefillStagePages - 1 || j == j1 - 1) {
-          // flush pages [jbase, j]: 8 threads per slot row, 4 pages per thread,
-          // so each group of 8 threads writes one contiguous run of the row
+        if ((j + 1) % kPrefillStagePages == 0 || j == j1 - 1) {
+          // flush pages [jbase, j]: one group of threads per slot row, 4 pages
+          // per thread, so each group writes one contiguous run of the row.
+          // Windows end at multiples of the window size, so in aligned rows a
+          // full window covers whole 64- or 128-byte lines.
           const int npg = j - jbase + 1;
           const int nvalid = (int)min((int64_t)kPrefillSlots, nslots - sbeg);
-          const int part = tid & 7;
+          constexpr int TPR = S::kFlushThreadsPerRow;
+          const int part = tid % TPR;
           const bool vec = a.vec_bs && (jbase & 3) == 0 && 4 * part + 3 < npg;
-          for (int sl = tid >> 3; sl < nvalid; sl += kThreads / 8) {
+          for (int sl = tid / TPR; sl < nvalid; sl += kThreads / TPR) {
             if (4 * part >= npg) continue;
             const uint32_t slot = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H)) + (uint32_t)sl;  // slot - H * row(sbeg)
             const uint32_t dr = slot / (uint32_t)a.H;
@@ -291,12 +304,17 @@ hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stre
   return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
 }
 
-int occupancy_prefill(int32_t q_dtype, int32_t page_size) {
+template <int QDT, int P>
+int occ_qp(bool bs, bool lg) {
+  return bs && lg ? occ_of(&k_prefill<QDT, P, true, true>)
+         : bs     ? occ_of(&k_prefill<QDT, P, true, false>)
+                  : occ_of(&k_prefill<QDT, P, false, true>);
+}
+
+int occupancy_prefill(int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
   if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_of(&k_prefill<MXS_Q_BF16, 128, true, false>)
-                            : occ_of(&k_prefill<MXS_Q_BF16, 64, true, false>);
-  return page_size == 128 ? occ_of(&k_prefill<MXS_Q_E4M3, 128, true, false>)
-                          : occ_of(&k_prefill<MXS_Q_E4M3, 64, true, false>);
+    return page_size == 128 ? occ_qp<MXS_Q_BF16, 128>(want_bs, want_lg) : occ_qp<MXS_Q_BF16, 64>(want_bs, want_lg);
+  return page_size == 128 ? occ_qp<MXS_Q_E4M3, 128>(want_bs, want_lg) : occ_qp<MXS_Q_E4M3, 64>(want_bs, want_lg);
 }
 
 }  // namespace mxs
