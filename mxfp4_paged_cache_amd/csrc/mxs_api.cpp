@@ -386,7 +386,10 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
     a.bs = bs->ptr;
     a.bs_row_stride = bs->row_stride;
     a.bs_head_stride = bs->head_stride;
-    a.vec_bs = aligned(bs->ptr, 16) && bs->row_stride % 4 == 0 && bs->head_stride % 4 == 0;
+    // widest store every block-score row allows: 16, 8 or 4 bytes
+    a.vec_bs = aligned(bs->ptr, 16) && bs->row_stride % 4 == 0 && bs->head_stride % 4 == 0  ? 4
+               : aligned(bs->ptr, 8) && bs->row_stride % 2 == 0 && bs->head_stride % 2 == 0 ? 2
+                                                                                             : 1;
   }
   if (want_lg) {
     a.lg = lg->ptr;

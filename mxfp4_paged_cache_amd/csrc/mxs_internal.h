@@ -61,7 +61,7 @@ struct KArgs {
   int32_t page_items;
   int32_t head_groups;
   int64_t items;
-  int32_t vec_bs;           // block-score rows 16-byte aligned (vector stores allowed)
+  int32_t vec_bs;           // widest vector store the block-score rows allow, in floats (4, 2 or 1)
   int32_t vec_lg;           // logit rows 16-byte aligned
 };
 

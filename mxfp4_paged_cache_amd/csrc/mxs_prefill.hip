@@ -242,38 +242,50 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
 #pragma unroll
           for (int n = 0; n < NQ; ++n) stage[((wave * NQ + n) * 16 + i) * kPrefillStageStride + (j - jbase)] = r[n] * s;
         }
-      }
-      __syncthreads();
-      if constexpr (WANT_BS) {
         if ((j + 1) % kPrefillStagePages == 0 || j == j1 - 1) {
-          // flush pages [jbase, j]: one group of threads per slot row, 4 pages
-          // per thread, so each group writes one contiguous run of the row.
-          // Windows end at multiples of the window size, so in aligned rows a
-          // full window covers whole 64- or 128-byte lines.
+          // Each wave flushes its own slot rows [wave * 16 NQ, +16 NQ) for pages
+          // [jbase, j]; no other wave touches them, so no workgroup barrier is
+          // needed (a wave's LDS accesses complete in order; the fences keep the
+          // compiler from moving its reads above its writes). A group of TPR
+          // lanes writes one contiguous run of a row, 4 pages per lane; windows
+          // end at multiples of the window size, so in aligned rows a full
+          // window covers whole 64- or 128-byte lines.
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           const int npg = j - jbase + 1;
-          const int nvalid = (int)min((int64_t)kPrefillSlots, nslots - sbeg);
           constexpr int TPR = S::kFlushThreadsPerRow;
-          const int part = tid % TPR;
-          const bool vec = a.vec_bs && (jbase & 3) == 0 && 4 * part + 3 < npg;
-          for (int sl = tid / TPR; sl < nvalid; sl += kThreads / TPR) {
+          const int part = lane % TPR;
+          const int lo = wave * NQ * 16;
+          const int hi = (int)min((int64_t)lo + NQ * 16, nslots - sbeg);
+          const bool full = 4 * part + 3 < npg;
+          const bool v4 = a.vec_bs == 4 && (jbase & 3) == 0 && full;
+          const bool v2 = a.vec_bs >= 2 && (jbase & 1) == 0 && full;
+          const uint32_t slot0 = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H));   // slot sbeg within its row
+          const int64_t rowb = (int64_t)row0 + sbeg / a.H;
+          for (int sl = lo + lane / TPR; sl < hi; sl += 64 / TPR) {
             if (4 * part >= npg) continue;
-            const uint32_t slot = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H)) + (uint32_t)sl;  // slot - H * row(sbeg)
+            const uint32_t slot = slot0 + (uint32_t)sl;
             const uint32_t dr = slot / (uint32_t)a.H;
-            const int64_t grow = (int64_t)row0 + sbeg / a.H + dr;
-            float* dst = a.bs + grow * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride + jbase +
-                         4 * part;
+            float* dst = a.bs + (rowb + dr) * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride +
+                         jbase + 4 * part;
             const float* src = stage + sl * kPrefillStageStride + 4 * part;
-            if (vec) {
+            if (v4) {
               const v4f v = {src[0], src[1], src[2], src[3]};
               *reinterpret_cast<v4f*>(dst) = v;
+            } else if (v2) {
+              typedef float v2f __attribute__((ext_vector_type(2)));
+              const v2f v0 = {src[0], src[1]}, v1 = {src[2], src[3]};
+              reinterpret_cast<v2f*>(dst)[0] = v0;
+              reinterpret_cast<v2f*>(dst)[1] = v1;
             } else {
               for (int x = 0; x < 4 && 4 * part + x < npg; ++x) dst[x] = src[x];
             }
           }
-          __syncthreads();
           jbase = j + 1;
         }
       }
+      __syncthreads();
     }
   }
 }
