@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxscore.so")
-SOURCES = [os.path.join(CSRC, "mxs_api.cpp"), os.path.join(CSRC, "mxs_decode.hip"), os.path.join(CSRC, "mxs_prefill.hip")]
+SOURCES = [os.path.join(CSRC, "mxs_api.cpp"), os.path.join(CSRC, "mxs_decode.hip"), os.path.join(CSRC, "mxs_prefill.hip"),
+           os.path.join(CSRC, "mxs_logits.hip")]
 HEADERS = [os.path.join(ROOT, "include", "mxscore.h"), os.path.join(CSRC, "mxs_internal.h"),
            os.path.join(CSRC, "mxs_device.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,11 +32,11 @@ FLAGS = [
 ]
 
 
-# The prefill kernels compare and fold finite scores (masked tokens are -inf,
+# The prefill and logits kernels compare and fold finite scores (masked tokens are -inf,
 # never NaN), so their translation unit is compiled without NaN semantics,
 # which removes NaN-quieting copies around the max folds of loop-carried
 # MFMA results. Decode runs measurably faster with default semantics.
-EXTRA_FLAGS = {"mxs_prefill.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"mxs_prefill.hip": ["-fno-honor-nans"], "mxs_logits.hip": ["-fno-honor-nans"]}
 
 
 def build(force: bool = True, verbose: bool = False) -> str:

@@ -160,24 +160,28 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
     p.items = lanes * p.page_items;
     p.grid = (int32_t)ceil_div(p.items, mxs::kWaves);
   } else {
-    // Work item = (request, block of query slots, chunk of pages). Enough
-    // items for a few per resident workgroup; the grid loops over them.
-    p.kernel = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+    // Work item = (request, block of query slots, chunk of pages); the grid
+    // loops over the items. Logits (asked for by either call) come from the
+    // logits kernel, block scores alone from the block-score kernel.
+    const bool lgk = mode == MXS_MODE_LOGITS || want_logits;
+    p.kernel = lgk ? mxs::KID_LOGITS : mxs::KID_PREFILL;
     p.head_groups = 1;
-    p.slots_per_item = mxs::prefill_slots(want_logits != 0);
+    p.slots_per_item = lgk ? mxs::kLogitsSlotsPerItem : mxs::kPrefillSlotsPerItem;
     const int64_t slots = (int64_t)p.max_query_len * num_heads;
     p.slot_items = (int32_t)(slots > 0 ? ceil_div(slots, p.slots_per_item) : 0);
     const int64_t base = (int64_t)batch * p.slot_items;
     int64_t grid = parallel_unit_num > 0 ? parallel_unit_num : capacity;
     if (parallel_unit_num <= 0 && grid >= 8) grid = grid / 8 * 8;
-    // pages per chunk for a chunk count (chunk starts stay 16-byte aligned in the score rows)
+    // pages per chunk for a chunk count: chunk starts stay 16-byte aligned
+    // in the score rows, and on 128-token output windows of the logits kernel
     auto ppi_for = [&](int64_t chunks) {
       int64_t ppi = NB > 0 ? ceil_div(NB, chunks) : 1;
       if (ppi > 4) ppi = ceil_div(ppi, 4) * 4;
+      if (lgk && page_size == 64) ppi = ceil_div(ppi, 2) * 2;
       return ppi;
     };
     int64_t ppi;
-    if (mode == MXS_MODE_PREFILL && !want_logits) {
+    if (!lgk) {
       // Block scores only: the grid strides over items ordered slot block
       // fastest. Pick the chunk count whose items spread most evenly over the
       // grid: the work is base * NB page-units, and the busiest workgroup
@@ -227,7 +231,9 @@ int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_
   if (q_dtype != MXS_Q_BF16 && q_dtype != MXS_Q_E4M3)
     return fail(MXS_EDTYPE, "query dtype must be bf16 or e4m3; got %d", q_dtype);
   if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
-  const int32_t kid = mode == MXS_MODE_DECODE ? mxs::KID_DECODE : mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+  const int32_t kid = mode == MXS_MODE_DECODE                    ? mxs::KID_DECODE
+                      : (mode == MXS_MODE_LOGITS || want_logits) ? mxs::KID_LOGITS
+                                                                 : mxs::KID_PREFILL;
   const int occ = occupancy_cached(dev, kid, q_dtype, page_size, want_blocks != 0, want_logits != 0);
   return mxs_plan_make_for(mode, q_dtype, page_size, num_heads, batch, max_query_len, max_seq_len, want_logits,
                            want_blocks, parallel_unit_num, info.cus, occ, plan);
@@ -265,9 +271,10 @@ bool plan_consistent(const mxs_plan& p, int mode, int32_t H, int32_t B, int32_t 
            p.pages_per_item <= mxs::kDecodeMaxPages && p.page_items % mxs::kWaves == 0 &&
            p.items == (int64_t)B * p.head_groups * p.page_items && (int64_t)p.grid * mxs::kWaves == p.items;
   }
-  const int32_t kid = mode == MXS_MODE_LOGITS ? mxs::KID_LOGITS : mxs::KID_PREFILL;
+  const bool lgk = mode == MXS_MODE_LOGITS || p.want_logits;
+  const int32_t kid = lgk ? mxs::KID_LOGITS : mxs::KID_PREFILL;
   const int64_t slots = (int64_t)max_query_len * H;
-  return p.kernel == kid && p.slots_per_item == mxs::prefill_slots(p.want_logits != 0) &&
+  return p.kernel == kid && p.slots_per_item == (lgk ? mxs::kLogitsSlotsPerItem : mxs::kPrefillSlotsPerItem) &&
          p.slot_items == (slots > 0 ? ceil_div(slots, p.slots_per_item) : 0) &&
          p.items == (int64_t)B * p.slot_items * p.page_items && p.grid <= (p.items > 0 ? p.items : 1);
 }

@@ -141,6 +141,40 @@ __device__ __forceinline__ void store_logits4(float* row, int t0, v4f v, int W, 
   }
 }
 
+// One page of K staged through registers into LDS by a whole workgroup.
+template <int P>
+struct PageStage {
+  static constexpr int kDataChunks = P * 64 / 16 / kThreads;   // 16-byte chunks per thread
+  u4 d[kDataChunks];
+  uint32_t sc;
+};
+
+// LDS layout of a staged page: the data of 16-token tile t is stored as
+// [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
+// a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
+// scales follow as [token][4 bytes] at P * 64. Thread tid fills LDS slot
+// s = tid + 256 c (16 bytes, contiguous writes) with global bytes
+// 16 g..16 g+15 of token 16 t + i, (t, g, i) = (s / 64, s / 16 % 4, s % 16):
+// a wave still loads one contiguous 1 KB tile per instruction.
+template <int P>
+__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
+    const int sl = tid + kThreads * c;
+    const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
+    st.d[c] = *reinterpret_cast<const u4*>(dp + off);
+  }
+  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+}
+
+template <int P>
+__device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
+#pragma unroll
+  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
+    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
+  if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace dev

@@ -1,5 +1,6 @@
 // Internal interface between the host entry points (mxs_api.cpp) and the
-// gfx950 kernels (mxs_kernels.hip). Not part of the public ABI.
+// gfx950 kernels (mxs_decode.hip, mxs_prefill.hip, mxs_logits.hip). Not part
+// of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,22 +13,21 @@ namespace mxs {
 // Kernel ids stored in mxs_plan::kernel.
 enum KernelId : int32_t {
   KID_DECODE = 1,     // one wave per (request, head group, page chunk); K straight to registers
-  KID_PREFILL = 2,    // workgroup per (request, slot block, page chunk); K staged in LDS
-  KID_LOGITS = 3,     // logits-first tiling (query as MFMA A operand, tokens along lanes)
+  KID_PREFILL = 2,    // block scores: workgroup per (request, 512 slots, page chunk); K staged in LDS
+  KID_LOGITS = 3,     // logits (+ block scores): workgroup per (request, 64 slots, page chunk); output via LDS windows
 };
 
 constexpr int kWaves = 4;           // waves per workgroup, every kernel
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPrefillTiles = 8;    // 16-slot query tiles per wave (prefill, block scores only)
-constexpr int kPrefillTilesLG = 4;  // 16-slot query tiles per wave (prefill writing logits)
-constexpr int kLogitsTiles = 4;     // 16-slot query tiles per wave (logits)
+constexpr int kPrefillTiles = 8;    // 16-slot query tiles per wave (block-score kernel)
+constexpr int kLogitsTiles = 1;     // 16-slot query tiles per wave (logits kernel)
 constexpr int kDecodeHeads = 64;    // heads per decode wave (4 tiles of 16)
 constexpr int kDecodeMaxPages = 32; // pages per decode wave (ids fit one VGPR; scores staged in LDS)
 constexpr int kDecodeStageStride = kDecodeMaxPages + 1;   // LDS row pitch in floats (odd: no bank conflicts)
 
-// Query slots per prefill work item: fewer when logits are written (those
-// variants need more registers for the logit row pointers).
-constexpr int prefill_slots(bool want_logits) { return kWaves * (want_logits ? kPrefillTilesLG : kPrefillTiles) * 16; }
+// Query slots per work item of the block-score and the logits kernel.
+constexpr int kPrefillSlotsPerItem = kWaves * kPrefillTiles * 16;
+constexpr int kLogitsSlotsPerItem = kWaves * kLogitsTiles * 16;
 
 // Everything a kernel needs, by value. Byte strides for query and cache,
 // element strides for int32 tables and fp32 outputs.
@@ -65,21 +65,26 @@ struct KArgs {
   int32_t vec_lg;           // logit rows 16-byte aligned
 };
 
-// Launchers (mxs_decode.hip, mxs_prefill.hip). Return the HIP status of the launch.
+// Launchers. Return the HIP status of the launch.
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
+hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 
 // Workgroups of the kernel variant (q dtype, page size, outputs) that fit on one CU.
 int occupancy_decode(int32_t q_dtype, int32_t page_size, bool want_lg);
-int occupancy_prefill(int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg);
+int occupancy_prefill(int32_t q_dtype, int32_t page_size);
+int occupancy_logits(int32_t q_dtype, int32_t page_size, bool want_bs);
 
 inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  return plan.kernel == KID_DECODE ? launch_decode(plan, a, stream) : launch_prefill(plan, a, stream);
+  return plan.kernel == KID_DECODE    ? launch_decode(plan, a, stream)
+         : plan.kernel == KID_PREFILL ? launch_prefill(plan, a, stream)
+                                      : launch_logits(plan, a, stream);
 }
 
 inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
-  return kernel == KID_DECODE ? occupancy_decode(q_dtype, page_size, want_lg)
-                              : occupancy_prefill(q_dtype, page_size, want_bs, want_lg);
+  return kernel == KID_DECODE    ? occupancy_decode(q_dtype, page_size, want_lg)
+         : kernel == KID_PREFILL ? occupancy_prefill(q_dtype, page_size)
+                                 : occupancy_logits(q_dtype, page_size, want_bs);
 }
 
 }  // namespace mxs

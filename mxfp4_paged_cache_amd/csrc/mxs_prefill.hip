@@ -1,4 +1,4 @@
-// Prefill / logits kernel of the paged MXFP4 index scorer (gfx950).
+// Prefill block-score kernel of the paged MXFP4 index scorer (gfx950).
 // Compiled without NaN semantics for float arithmetic (see the build): the
 // kernel only compares and folds finite scores and -inf.
 #include "mxs_device.h"
@@ -8,78 +8,33 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
-// Prefill (also the logits path for now): one workgroup per work item
-// (request, block of 256 query slots, chunk of pages), looping over items
-// with a grid stride. A query slot is (row, head); slot = row * H + head, so
-// a 16-slot tile is 16 heads of one row when H is a multiple of 16. Each wave
-// keeps 4 query tiles in registers for the whole item; every page is staged
-// once per workgroup in LDS (double-buffered, 8.5 KB per buffer at P = 128)
-// and read by all four waves. Block scores are staged in LDS for up to 32
-// pages and leave as contiguous per-slot rows.
+// Prefill block scores: one workgroup per work item (request, block of 512
+// query slots, chunk of pages), looping over items with a grid stride. A
+// query slot is (row, head); slot = row * H + head, so a 16-slot tile is 16
+// heads of one row when H is a multiple of 16. Each wave keeps 8 query tiles
+// in registers for the whole item; every page is staged once per workgroup in
+// LDS (double-buffered, 8.5 KB per buffer at P = 128) and read by all four
+// waves. Block scores are staged in LDS for up to 16 pages and leave as
+// contiguous per-slot rows.
 //
-// Block-score work items are ordered slot block fastest: at any moment the
-// whole grid works on one chunk of pages (small enough for every XCD's L2),
-// and each workgroup's items are spread over all query rows and all chunks,
-// so the causal triangle (chunks past some rows' limits are cheap) costs
-// every workgroup the same. When logits are written, items are ordered page
-// chunk fastest instead: with a grid and a chunk count that are both
-// multiples of 8, workgroup c only sees chunks c mod 8 (workgroups go
-// round-robin over the 8 XCDs), so each XCD keeps one eighth of the pages in
-// its own L2.
+// Work items are ordered slot block fastest: at any moment the whole grid
+// works on one chunk of pages (small enough for every XCD's L2), and each
+// workgroup's items are spread over all query rows and all chunks, so the
+// causal triangle (chunks past some rows' limits are cheap) costs every
+// workgroup the same.
 // ---------------------------------------------------------------------------
-template <int P>
-struct PageStage {
-  static constexpr int kDataChunks = P * 64 / 16 / kThreads;   // 16-byte chunks per thread
-  u4 d[kDataChunks];
-  uint32_t sc;
-};
-
-// LDS layout of a staged page: the data of 16-token tile t is stored as
-// [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
-// a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
-// scales follow as [token][4 bytes] at P * 64. Thread tid fills LDS slot
-// s = tid + 256 c (16 bytes, contiguous writes) with global bytes
-// 16 g..16 g+15 of token 16 t + i, (t, g, i) = (s / 64, s / 16 % 4, s % 16):
-// a wave still loads one contiguous 1 KB tile per instruction.
-template <int P>
-__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
-#pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
-    const int sl = tid + kThreads * c;
-    const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
-    st.d[c] = *reinterpret_cast<const u4*>(dp + off);
-  }
-  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
-}
-
-template <int P>
-__device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
-#pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
-    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
-  if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
-}
-
-// Per-variant shape: query tiles per wave, slots per item, and the block-score
-// staging (pages per flush; LDS row pitch odd, so no bank conflicts). With 8
-// tiles a flush window is 16 pages, which keeps two workgroups per CU in LDS.
-template <bool WANT_LG>
-struct PrefillShape {
-  static constexpr int NQ = WANT_LG ? kPrefillTilesLG : kPrefillTiles;
-  static constexpr int kSlots = kWaves * NQ * 16;
-  static constexpr int kStagePages = WANT_LG ? 32 : 16;
-  static constexpr int kStageStride = kStagePages + 1;
-  static constexpr int kFlushThreadsPerRow = kStagePages / 4;   // 4 pages per thread
-};
+constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;   // query slots per work item
+constexpr int kPrefillStagePages = 16;                        // pages per block-score flush
+constexpr int kPrefillStageStride = kPrefillStagePages + 1;   // LDS row pitch (odd: no bank conflicts)
+constexpr int kFlushLanesPerRow = kPrefillStagePages / 4;     // 4 pages per lane
 
 // Score one LDS-resident page against this wave's query tiles; r[n] gets the
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
 // The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
 // most two tiles of MFMA results are live.
-template <int P, int NQ, bool MASK, bool LG>
-__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[NQ], const int (&lrel)[NQ], int j,
-                                             int g, int i, float (&r)[NQ], float* const (&lrow)[NQ],
-                                             const KArgs& a) {
+template <int P, int NQ, bool MASK>
+__device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[NQ], const int (&lrel)[NQ], int g,
+                                             int i, float (&r)[NQ]) {
   constexpr int TPP = P / 16;
   const uint8_t* kdl = kb + g * 256 + i * 16;     // this lane's 16 bytes of tile t: kdl + 1024 t
   const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
@@ -99,9 +54,6 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
         for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel[n]) ? c[v] : kNegInf;
       }
       m[n] = max_into(m[n], c);
-      if constexpr (LG) {
-        if (lrow[n]) store_logits4(lrow[n], j * P + 16 * t + 4 * g, c * a.sm_scale, a.max_seq_len, a.vec_lg);
-      }
     }
   };
   // two tiles per trip, no MFMA result carried across trips; the next pair of
@@ -128,35 +80,22 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
   for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
 }
 
-template <int QDT, int P, bool WANT_BS, bool WANT_LG>
+template <int QDT, int P>
 __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
-  using S = PrefillShape<WANT_LG>;
-  constexpr int NQ = S::NQ;
-  constexpr int kPrefillSlots = S::kSlots;
-  constexpr int kPrefillStagePages = S::kStagePages;
-  constexpr int kPrefillStageStride = S::kStageStride;
+  constexpr int NQ = kPrefillTiles;
   constexpr int PB = P * 68;   // bytes of one staged page
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
-  __shared__ float stage[WANT_BS ? kPrefillSlots * kPrefillStageStride : 1];
+  __shared__ float stage[kPrefillSlots * kPrefillStageStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   const float s = a.sm_scale;
-  const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
 
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
-    int pc, sb, b;
-    if constexpr (WANT_LG) {
-      pc = (int)(item % a.page_items);
-      const int64_t rest = item / a.page_items;
-      sb = (int)(rest % a.slot_items);
-      b = (int)(rest / a.slot_items);
-    } else {
-      sb = (int)(item % a.slot_items);
-      const int64_t rest = item / a.slot_items;
-      pc = (int)(rest % a.page_items);
-      b = (int)(rest / a.page_items);
-    }
+    const int sb = (int)(item % a.slot_items);
+    const int64_t rest = item / a.slot_items;
+    const int pc = (int)(rest % a.page_items);
+    const int b = (int)(rest / a.page_items);
     const int row0 = a.cu[b];
     const int qlen = a.cu[b + 1] - row0;
     const int64_t nslots = (int64_t)qlen * a.H;
@@ -169,7 +108,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     // this lane's query slots
     v8i qt[NQ];
     int lim[NQ];
-    float* lrow[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       const int64_t sl = sbeg + (int64_t)(wave * NQ + n) * 16 + i;
@@ -180,7 +118,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       const int64_t grow = (int64_t)row0 + r;
       lim[n] = valid ? clampi(min(seq, pre + r + 1), 0, a.max_seq_len) : 0;
       qt[n] = load_q_tile_masked<QDT>(a.q + grow * a.q_row_stride + (int64_t)h * a.q_head_stride, g, valid);
-      lrow[n] = (WANT_LG && valid) ? a.lg + grow * a.lg_row_stride + (int64_t)h * a.lg_head_stride : nullptr;
     }
     // smallest limit among this wave's slots: the limit of its first slot
     const int64_t wfirst = sbeg + (int64_t)wave * NQ * 16;
@@ -222,22 +159,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) lrel[n] = lim[n] - j * P - 4 * g;
         if ((j + 1) * P > wave_min_lim)
-          prefill_page<P, NQ, true, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+          prefill_page<P, NQ, true>(kb, qt, lrel, g, i, r);
         else
-          prefill_page<P, NQ, false, WANT_LG>(kb, qt, lrel, j, g, i, r, lrow, a);
+          prefill_page<P, NQ, false>(kb, qt, lrel, g, i, r);
         if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
       } else {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) r[n] = kNegInf;
-        if constexpr (WANT_LG) {
-#pragma unroll
-          for (int n = 0; n < NQ; ++n)
-            if (lrow[n])
-#pragma unroll
-              for (int t = 0; t < P / 16; ++t) store_logits4(lrow[n], j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
-        }
       }
-      if constexpr (WANT_BS) {
+      {
         if (g == 0) {
 #pragma unroll
           for (int n = 0; n < NQ; ++n) stage[((wave * NQ + n) * 16 + i) * kPrefillStageStride + (j - jbase)] = r[n] * s;
@@ -254,7 +184,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           const int npg = j - jbase + 1;
-          constexpr int TPR = S::kFlushThreadsPerRow;
+          constexpr int TPR = kFlushLanesPerRow;
           const int part = lane % TPR;
           const int lo = wave * NQ * 16;
           const int hi = (int)min((int64_t)lo + NQ * 16, nslots - sbeg);
@@ -301,11 +231,8 @@ int occ_of(K kernel) {
 template <int QDT, int P>
 hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<KArgs*>(&a)};
-  const bool bs = a.bs != nullptr, lg = a.lg != nullptr;
-  const void* fn = bs && lg ? reinterpret_cast<const void*>(&k_prefill<QDT, P, true, true>)
-                   : bs     ? reinterpret_cast<const void*>(&k_prefill<QDT, P, true, false>)
-                            : reinterpret_cast<const void*>(&k_prefill<QDT, P, false, true>);
-  return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&k_prefill<QDT, P>), dim3(plan.grid), dim3(kThreads), args, 0,
+                         stream);
 }
 
 }  // namespace
@@ -316,17 +243,10 @@ hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stre
   return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
 }
 
-template <int QDT, int P>
-int occ_qp(bool bs, bool lg) {
-  return bs && lg ? occ_of(&k_prefill<QDT, P, true, true>)
-         : bs     ? occ_of(&k_prefill<QDT, P, true, false>)
-                  : occ_of(&k_prefill<QDT, P, false, true>);
-}
-
-int occupancy_prefill(int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
+int occupancy_prefill(int32_t q_dtype, int32_t page_size) {
   if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_qp<MXS_Q_BF16, 128>(want_bs, want_lg) : occ_qp<MXS_Q_BF16, 64>(want_bs, want_lg);
-  return page_size == 128 ? occ_qp<MXS_Q_E4M3, 128>(want_bs, want_lg) : occ_qp<MXS_Q_E4M3, 64>(want_bs, want_lg);
+    return page_size == 128 ? occ_of(&k_prefill<MXS_Q_BF16, 128>) : occ_of(&k_prefill<MXS_Q_BF16, 64>);
+  return page_size == 128 ? occ_of(&k_prefill<MXS_Q_E4M3, 128>) : occ_of(&k_prefill<MXS_Q_E4M3, 64>);
 }
 
 }  // namespace mxs
