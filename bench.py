@@ -56,8 +56,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_name(mode: str) -> str:
-    return "k_decode" if mode == "decode" else "k_prefill"
+def kernel_name(wl) -> str:
+    """The kernel a workload runs: decode, the block-score kernel, or the logits
+    kernel (every call that writes logits)."""
+    if wl.mode == "decode":
+        return "k_decode"
+    return "k_logits" if (wl.mode == "logits" or wl.want_logits) else "k_prefill"
 
 
 def kernel_source_hash() -> str:
@@ -73,8 +77,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_path(mode: str, workload: str) -> str:
-    return os.path.join(PROFILES, f"{kernel_name(mode)}_{workload}_traffic.json")
+def traffic_path(wl) -> str:
+    return os.path.join(PROFILES, f"{kernel_name(wl)}_{wl.name}_traffic.json")
 
 
 def pmc_summary(dbs):
@@ -87,8 +91,8 @@ def pmc_summary(dbs):
         per = {}
         for name, disp, val, kname in con.execute(
                 "select counter_name, dispatch_id, value, kernel_name from counters_collection"):
-            kind = "copy" if "neg" in kname else ("k_decode" if "k_decode" in kname else
-                                                  ("k_prefill" if "k_prefill" in kname else None))
+            kind = "copy" if "neg" in kname else next((k for k in ("k_decode", "k_prefill", "k_logits") if k in kname),
+                                                      None)
             if kind is None:
                 continue
             per.setdefault((name, kind), {}).setdefault(disp, 0.0)
@@ -98,7 +102,7 @@ def pmc_summary(dbs):
     out = {}
     for counter, field in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         copy = acc.get((counter, "copy"))
-        for k in ("k_decode", "k_prefill"):
+        for k in ("k_decode", "k_prefill", "k_logits"):
             v = acc.get((counter, k))
             if v is None or not copy:
                 continue
@@ -145,8 +149,8 @@ def main():
     if args.pmc_summary:
         from mxfp4_paged_cache_amd import workloads as W
         wl = W.CONFIGS[args.config]()
-        rec = pmc_summary(args.pmc_summary).get(kernel_name(wl.mode), {})
-        rec = {"workload": wl.name, "kernel": kernel_name(wl.mode), "source_hash": kernel_source_hash(),
+        rec = pmc_summary(args.pmc_summary).get(kernel_name(wl), {})
+        rec = {"workload": wl.name, "kernel": kernel_name(wl), "source_hash": kernel_source_hash(),
                "copy_probe_bytes": COPY_PROBE_BYTES, **rec}
         if "read" in rec and "write" in rec:
             rec["bytes_per_launch"] = rec["read"]["bytes"] + rec["write"]["bytes"]
@@ -251,7 +255,7 @@ def main():
     tflops = flops / (ms / 1e3) / 1e12
     hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64)
     traffic = None
-    tpath = args.traffic or traffic_path(wl.mode, wl.name)
+    tpath = args.traffic or traffic_path(wl)
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
@@ -296,7 +300,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
         "timing": "eager launches" if graph is None else "graph replay of the timed steps",
-        "kernel": kernel_name(wl.mode),
+        "kernel": kernel_name(wl),
     }
     print(json.dumps(line), flush=True)
 
