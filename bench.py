@@ -65,10 +65,11 @@ def kernel_name(wl) -> str:
 
 
 def kernel_source_hash() -> str:
-    """Hash of everything that determines the kernels' machine code."""
+    """Hash of everything the kernels are compiled from (device sources, the
+    headers they include, the build flags); host-only code is left out."""
     pkg = os.path.join(ROOT, "mxfp4_paged_cache_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py"),
-                                                                 os.path.join(ROOT, "include", "mxscore.h")]
+    files = (sorted(glob.glob(os.path.join(pkg, "csrc", "*.hip")) + glob.glob(os.path.join(pkg, "csrc", "*.h"))) +
+             [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "mxscore.h")])
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -316,7 +317,11 @@ def cpu_baseline(wl, inp, sample_rows: int):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
     T = wl.T
     if sample_rows <= 0:
-        sample_rows = {"decode": 16}.get(wl.mode, 4)
+        # about 10 s of oracle work: ~7e6 live triples per core-second measured
+        # for this oracle, so ~1.1e9 triples on 16 cores
+        per_row = max(1, (sum(wl.limits()) * wl.H) // max(T, 1))
+        budget = int(7e6 * threads * 10)
+        sample_rows = max(1, min(T, budget // per_row))
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(T, size=min(sample_rows, T), replace=False)).astype(np.int32)
     lim = wl.limits()

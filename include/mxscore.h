@@ -196,6 +196,23 @@ int mxs_score_decode(const mxs_query* q, const mxs_kcache* k, const mxs_batch* b
 int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
                      const mxs_out* logits, const mxs_out* block_scores, const mxs_plan* plan, void* stream);
 
+/* Check of the device-side contract that the scoring calls cannot verify
+ * without a device-to-host copy (see "Device contract" above). Synchronous:
+ * copies the request metadata (and, with check_scales, the scale bytes of
+ * every live token) to host memory after the work already queued on stream,
+ * and checks, for mode MXS_MODE_PREFILL / MXS_MODE_LOGITS:
+ *   cu_seqlens_q[0] == 0, non-decreasing, cu_seqlens_q[batch] == total_rows,
+ *   every request's q_len <= max_query_len, prefix_lens >= 0;
+ * for every mode:
+ *   0 <= seq_lens[b] <= max_seq_len;
+ *   block-table entries of live pages (pages holding a token some row of the
+ *   request sees) in [0, num_pages);
+ *   with check_scales != 0: e8m0 bytes of live tokens in [1, 254].
+ * Returns MXS_OK, or MXS_EINVAL naming the first violation (mxs_last_error),
+ * or MXS_EDEVICE if a copy fails. For tests and debugging: not on the hot
+ * path and not capturable in a graph. Allocates host memory only. */
+int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* batch, int32_t check_scales, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* mxs_last_error(void);
 

@@ -73,7 +73,7 @@ class Plan(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("mxs_plan_make", "mxs_plan_make_for", "mxs_score_prefill", "mxs_score_decode", "mxs_score_logits",
-           "mxs_last_error", "mxs_version")
+           "mxs_check_metadata", "mxs_last_error", "mxs_version")
 
 
 def library_path() -> str:
@@ -97,6 +97,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [P(Query), P(KCache), P(Batch), ctypes.c_float, P(Out), P(Out), P(Plan), ctypes.c_void_p]
             f.restype = ctypes.c_int
+        L.mxs_check_metadata.argtypes = [i32, P(KCache), P(Batch), i32, ctypes.c_void_p]
+        L.mxs_check_metadata.restype = ctypes.c_int
         L.mxs_last_error.restype = ctypes.c_char_p
         L.mxs_last_error.argtypes = []
         L.mxs_version.restype = ctypes.c_char_p
@@ -282,3 +284,24 @@ def score_decode(q, k_data, k_scale, block_table, seq_lens, max_seq_len: int, sm
                                       ctypes.byref(bo), ctypes.byref(lo),
                                       ctypes.byref(plan) if plan is not None else None, _stream(dev, stream)))
     return (out, lg) if want_lg else out
+
+
+def check_metadata(mode: str, k_data, k_scale, block_table, seq_lens, max_seq_len: int, cu_seqlens_q=None,
+                   prefix_lens=None, max_query_len: int = 0, check_scales: bool = False, stream=None) -> None:
+    """Synchronous host check of the device-side contract (request metadata,
+    live block-table entries, optionally live e8m0 bytes); raises ValueError
+    naming the first violation. For tests and debugging, not the hot path."""
+    m = {"prefill": MXS_MODE_PREFILL, "decode": MXS_MODE_DECODE, "logits": MXS_MODE_LOGITS}[mode]
+    dev = _same_device(k_data, k_scale, block_table, seq_lens, cu_seqlens_q, prefix_lens)
+    kc = _kcache(k_data, k_scale)
+    B = seq_lens.shape[0]
+    btp, bts, btw = _table(block_table)
+    if m == MXS_MODE_DECODE:
+        ba = Batch(btp, bts, btw, None, _int_vec("seq_lens", seq_lens, B), None, B, B, 1, int(max_seq_len))
+    else:
+        total = int(cu_seqlens_q[-1].item()) if B > 0 else 0
+        ba = Batch(btp, bts, btw, _int_vec("cu_seqlens_q", cu_seqlens_q, B + 1), _int_vec("seq_lens", seq_lens, B),
+                   _int_vec("prefix_lens", prefix_lens, B), B, total, int(max_query_len), int(max_seq_len))
+    with torch.cuda.device(dev):
+        _check(lib().mxs_check_metadata(m, ctypes.byref(kc), ctypes.byref(ba), int(bool(check_scales)),
+                                        _stream(dev, stream)))

@@ -9,7 +9,9 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <algorithm>
 #include <mutex>
+#include <vector>
 #include <string>
 
 #include "mxs_internal.h"
@@ -99,6 +101,85 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 extern "C" {
 
 const char* mxs_last_error(void) { return g_error.c_str(); }
+
+int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, int32_t check_scales, void* stream) {
+  if (!k || !bt) return fail(MXS_EINVAL, "cache and batch descriptors must not be NULL");
+  if (mode != MXS_MODE_PREFILL && mode != MXS_MODE_DECODE && mode != MXS_MODE_LOGITS)
+    return fail(MXS_EINVAL, "unknown mode %d", mode);
+  if (k->page_size != 64 && k->page_size != 128)
+    return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", k->page_size);
+  const bool decode = mode == MXS_MODE_DECODE;
+  const int32_t B = bt->batch, P = k->page_size;
+  if (B < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  if (B == 0) return MXS_OK;
+  if (!bt->block_table || !bt->seq_lens || (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens)))
+    return fail(MXS_EINVAL, "metadata pointers must not be NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto copy = [&](void* dst, const void* src, size_t n) {
+    return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToHost, st) == hipSuccess;
+  };
+  std::vector<int32_t> seq(B), cu(decode ? 0 : B + 1), pre(decode ? 0 : B);
+  if (!copy(seq.data(), bt->seq_lens, 4 * (size_t)B) ||
+      (!decode && (!copy(cu.data(), bt->cu_seqlens_q, 4 * (size_t)(B + 1)) ||
+                   !copy(pre.data(), bt->prefix_lens, 4 * (size_t)B))) ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(MXS_EDEVICE, "copying the request metadata failed");
+  if (!decode) {
+    if (cu[0] != 0) return fail(MXS_EINVAL, "cu_seqlens_q[0] is %d, not 0", cu[0]);
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t ql = (int64_t)cu[b + 1] - cu[b];
+      if (ql < 0) return fail(MXS_EINVAL, "cu_seqlens_q decreases at request %d", b);
+      if (ql > bt->max_query_len)
+        return fail(MXS_EINVAL, "request %d has %lld query rows, more than max_query_len %d", b, (long long)ql,
+                    bt->max_query_len);
+      if (pre[b] < 0) return fail(MXS_EINVAL, "prefix_lens[%d] is negative (%d)", b, pre[b]);
+    }
+    if (cu[B] != bt->total_rows)
+      return fail(MXS_EINVAL, "cu_seqlens_q[batch] is %d, total_rows is %d", cu[B], bt->total_rows);
+  }
+  // live tokens of each request: the largest limit over its rows
+  std::vector<int64_t> live(B);
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq[b] < 0 || seq[b] > bt->max_seq_len)
+      return fail(MXS_EINVAL, "seq_lens[%d] is %d, outside [0, max_seq_len = %d]", b, seq[b], bt->max_seq_len);
+    int64_t lim = seq[b];
+    if (!decode) {
+      const int64_t ql = (int64_t)cu[b + 1] - cu[b];
+      lim = ql > 0 ? std::min<int64_t>(seq[b], (int64_t)pre[b] + ql) : 0;
+    }
+    live[b] = lim;
+  }
+  std::vector<int32_t> row;
+  std::vector<uint8_t> sc;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t pages = ceil_div(live[b], P);
+    if (pages == 0) continue;
+    if (pages > bt->bt_width)
+      return fail(MXS_EINVAL, "request %d has %lld live pages, more than the block table width %d", b,
+                  (long long)pages, bt->bt_width);
+    row.resize(pages);
+    if (!copy(row.data(), bt->block_table + (int64_t)b * bt->bt_row_stride, 4 * (size_t)pages) ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return fail(MXS_EDEVICE, "copying block-table row %d failed", b);
+    for (int64_t j = 0; j < pages; ++j)
+      if (row[j] < 0 || row[j] >= k->num_pages)
+        return fail(MXS_EINVAL, "block_table[%d][%lld] = %d is outside [0, num_pages = %lld) for a live page", b,
+                    (long long)j, row[j], (long long)k->num_pages);
+    if (!check_scales) continue;
+    sc.resize((size_t)P * 4);
+    for (int64_t j = 0; j < pages; ++j) {
+      if (!copy(sc.data(), static_cast<const uint8_t*>(k->scale) + (int64_t)row[j] * k->scale_page_stride, sc.size()) ||
+          hipStreamSynchronize(st) != hipSuccess)
+        return fail(MXS_EDEVICE, "copying the scales of page %d failed", row[j]);
+      const int64_t ntok = std::min<int64_t>(P, live[b] - j * P);
+      for (int64_t t = 0; t < ntok * 4; ++t)
+        if (sc[t] == 0 || sc[t] == 255)
+          return fail(MXS_EINVAL, "request %d, token %lld: e8m0 byte %d outside [1, 254]", b,
+                      (long long)(j * P + t / 4), sc[t]);
+    }
+  }
+  return MXS_OK;
+}
 
 const char* mxs_version(void) { return "mxscore 0.1 (gfx950)"; }
 

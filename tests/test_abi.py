@@ -184,6 +184,22 @@ def test_plan_rejections(L):
     assert plan_for(L, mx.MXS_MODE_LOGITS, lg=0)[0] == mx.MXS_EINVAL
 
 
+def test_check_metadata_rejections_before_any_copy(L):
+    q, k, b, bs, lg = valid_args()
+    assert L.mxs_check_metadata(9, ctypes.byref(k), ctypes.byref(b), 0, None) == mx.MXS_EINVAL
+    assert L.mxs_check_metadata(mx.MXS_MODE_PREFILL, None, ctypes.byref(b), 0, None) == mx.MXS_EINVAL
+    bad = mx.KCache.from_buffer_copy(bytes(k))
+    bad.page_size = 32
+    assert L.mxs_check_metadata(mx.MXS_MODE_PREFILL, ctypes.byref(bad), ctypes.byref(b), 0, None) == mx.MXS_ELAYOUT
+    empty = mx.Batch.from_buffer_copy(bytes(b))
+    empty.batch = 0
+    assert L.mxs_check_metadata(mx.MXS_MODE_DECODE, ctypes.byref(k), ctypes.byref(empty), 1, None) == mx.MXS_OK
+    nulls = mx.Batch.from_buffer_copy(bytes(b))
+    nulls.seq_lens = None
+    assert L.mxs_check_metadata(mx.MXS_MODE_DECODE, ctypes.byref(k), ctypes.byref(nulls), 0, None) == mx.MXS_EINVAL
+    assert b"NULL" in L.mxs_last_error()
+
+
 def test_python_layer_rejects_cpu_tensors():
     import torch
     q = torch.zeros((1, 1, 128), dtype=torch.bfloat16)

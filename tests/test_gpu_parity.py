@@ -57,26 +57,43 @@ def test_decode_ragged(P, qdt):
     check_case(wl, seed=2)
 
 
+# Prefill cases run twice: block scores alone (the block-score kernel) and
+# with logits (the logits kernel, which also returns the block scores).
+LOGITS = pytest.mark.parametrize("lg", [False, True], ids=["blocks", "logits"])
+
+
+@LOGITS
 @pytest.mark.parametrize("H", [1, 2, 3, 17, 64])
 @pytest.mark.parametrize("P", [64, 128])
-def test_prefill_ragged_heads(H, P):
+def test_prefill_ragged_heads(H, P, lg):
     # mixed query lengths with an empty request, prefixes mid-page, heads that
     # are not a multiple of the 16-slot tile (tiles straddle rows)
     wl = W.Workload("prefill_ragged", "prefill", H=H, page_size=P, q_lens=[5, 0, 17, 1], prefix_lens=[70, 3, 100, 0],
-                    seq_lens=[75, 3, 117, 1], want_logits=True, max_seq_len=200)
+                    seq_lens=[75, 3, 117, 1], want_logits=lg, max_seq_len=200)
     check_case(wl, seed=3 + H)
 
 
-def test_prefill_e4m3_query_long_rows():
+@LOGITS
+def test_prefill_many_rows_ragged_pages(lg):
+    # more than one work item along slots and pages, a window that is not a
+    # multiple of the page size and limits that end mid-page
+    wl = W.Workload("prefill_many_rows", "prefill", H=24, page_size=64, q_lens=[37, 70], prefix_lens=[1000, 515],
+                    seq_lens=[1037, 585], want_logits=lg, max_seq_len=1100)
+    check_case(wl, seed=12)
+
+
+@LOGITS
+def test_prefill_e4m3_query_long_rows(lg):
     wl = W.Workload("prefill_e4m3", "prefill", H=64, page_size=128, q_lens=[40], prefix_lens=[2000],
-                    seq_lens=[2040], q_dtype="e4m3", want_logits=True)
+                    seq_lens=[2040], q_dtype="e4m3", want_logits=lg)
     check_case(wl, seed=4)
 
 
-def test_wide_scale_bytes():
+@LOGITS
+def test_wide_scale_bytes(lg):
     # e8m0 bytes 100..150 (outside the e4m3-exact window [119, 133])
     wl = W.Workload("prefill_wide_scales", "prefill", H=64, page_size=128, q_lens=[24], prefix_lens=[700],
-                    seq_lens=[724], scale_lo=100, scale_hi=150, want_logits=True)
+                    seq_lens=[724], scale_lo=100, scale_hi=150, want_logits=lg)
     check_case(wl, seed=5, min_exact=0.60)
 
 
@@ -89,9 +106,10 @@ def test_logits_shared_region_small():
     check_case(wl, seed=6)
 
 
-def test_strided_query():
+@LOGITS
+def test_strided_query(lg):
     wl = W.Workload("prefill_strided_q", "prefill", H=16, page_size=128, q_lens=[9], prefix_lens=[250],
-                    seq_lens=[259], want_logits=True)
+                    seq_lens=[259], want_logits=lg)
     check_case(wl, seed=7, q_strided=True)
 
 
@@ -123,7 +141,8 @@ def test_e4m3_conversion_exhaustive():
 
 def test_cross_mode_bitwise():
     # decode == prefill with one row per request (prefix = seq_len - 1) ==
-    # logits mode, element for element; block score == max of the logits.
+    # logits mode, element for element, and the block scores of all three
+    # kernels agree bitwise; block score == max of the logits.
     seq = [700, 129, 64, 1]
     B = len(seq)
     wd = W.Workload("xm_decode", "decode", H=64, page_size=128, q_lens=[1] * B, prefix_lens=[s - 1 for s in seq],
@@ -134,12 +153,14 @@ def test_cross_mode_bitwise():
     dev.wl = W.Workload("xm_prefill", "prefill", H=64, page_size=128, q_lens=[1] * B,
                         prefix_lens=[s - 1 for s in seq], seq_lens=seq, want_logits=True, max_seq_len=768)
     bs_p, lg_p = run_gpu(dev, want_logits=True)
+    bs_b, _ = run_gpu(dev, want_logits=False)
     dev.wl = W.Workload("xm_logits", "logits", H=64, page_size=128, q_lens=[1] * B,
                         prefix_lens=[s - 1 for s in seq], seq_lens=seq, want_logits=True, want_blocks=True,
                         max_seq_len=768)
     bs_l, lg_l = run_gpu(dev)
     torch.cuda.synchronize()
     for a, b_, n in [(bs_d, bs_p, "decode/prefill blocks"), (bs_d, bs_l, "decode/logits blocks"),
+                     (bs_d, bs_b, "decode/block-score kernel"),
                      (lg_d, lg_p, "decode/prefill logits"), (lg_d, lg_l, "decode/logits logits")]:
         assert torch.equal(a.view(torch.int32), b_.view(torch.int32)), n
     mx_of_logits = lg_d.view(B, 64, 6, 128).amax(dim=3)
@@ -181,6 +202,16 @@ def test_explicit_plans_give_identical_outputs():
         p = mx.make_plan("decode", torch.bfloat16, 64, 64, 3, 1, 4000, False, True, pun)
         other, _ = run_gpu(dev, plan=p)
         assert torch.equal(base.view(torch.int32), other.view(torch.int32)), pun
+    wl = W.Workload("plans_l", "logits", H=20, page_size=64, q_lens=[30, 9], prefix_lens=[600, 40],
+                    seq_lens=[630, 49], want_logits=True, want_blocks=True)
+    host = W.make_inputs(wl, 13, "cpu")
+    dev = gpu_inputs(host)
+    base_bs, base_lg = run_gpu(dev)
+    for pun in (1, 3, 17, 500):
+        p = mx.make_plan("logits", torch.bfloat16, 64, 20, 2, 30, 630, True, True, pun)
+        obs, olg = run_gpu(dev, plan=p)
+        assert torch.equal(base_lg.view(torch.int32), olg.view(torch.int32)), pun
+        assert torch.equal(base_bs.view(torch.int32), obs.view(torch.int32)), pun
 
 
 def test_graph_replay_with_poisoned_outputs():
@@ -272,6 +303,48 @@ def test_rejections_on_gpu_tensors():
         setattr(bad, field, val)
         with pytest.raises(ValueError):
             mx.score_prefill(q, kd, ks, bt, cu, sl, pl, 1, 256, S, plan=bad)
+
+
+def test_check_metadata_finds_contract_violations():
+    wl = W.Workload("meta", "prefill", H=8, page_size=64, q_lens=[3, 0, 5], prefix_lens=[100, 7, 60],
+                    seq_lens=[103, 7, 65], max_seq_len=160, table_pad=2)
+    host = W.make_inputs(wl, 14, "cpu")
+    dev = gpu_inputs(host)
+    args = dict(cu_seqlens_q=dev.cu_seqlens_q, prefix_lens=dev.prefix_lens, max_query_len=5)
+    mx.check_metadata("prefill", dev.k_data, dev.k_scale, dev.block_table, dev.seq_lens, 160, check_scales=True,
+                      **args)
+    mx.check_metadata("decode", dev.k_data, dev.k_scale, dev.block_table, dev.seq_lens, 160, check_scales=True)
+
+    def expect(msg, **over):
+        kw = dict(block_table=dev.block_table, seq_lens=dev.seq_lens, k_scale=dev.k_scale, **args)
+        kw.update(over)
+        with pytest.raises(ValueError, match=msg):
+            mx.check_metadata("prefill", dev.k_data, kw.pop("k_scale"), kw.pop("block_table"), kw.pop("seq_lens"), 160,
+                              check_scales=True, **kw)
+
+    bt = dev.block_table.clone()
+    bt[2, 1] = host.k_data.shape[0]          # live page of request 2 out of range
+    expect("outside", block_table=bt)
+    bt = dev.block_table.clone()
+    bt[0, 1] = -1                            # request 0 sees tokens 0..102: page 1 is live
+    expect("outside", block_table=bt)
+    bt = dev.block_table.clone()
+    bt[0, 2] = -1                            # page 2 of request 0 holds no live token: padding is fine
+    mx.check_metadata("prefill", dev.k_data, dev.k_scale, bt, dev.seq_lens, 160, **args)
+    expect("seq_lens", seq_lens=torch.tensor([103, 7, 200], dtype=torch.int32, device="cuda"))
+    expect("decreases", cu_seqlens_q=torch.tensor([0, 3, 2, 8], dtype=torch.int32, device="cuda"))
+    expect("max_query_len", max_query_len=4)
+    ks = dev.k_scale.clone()
+    page = int(dev.block_table[2, 0])
+    ks[page, 5, 1] = 0                       # live token 5 of request 2
+    expect("e8m0", k_scale=ks)
+    ks = dev.k_scale.clone()
+    ks[page, 63, 3] = 255                    # token 63 of request 2 (limit 65): live
+    expect("e8m0", k_scale=ks)
+    ks = dev.k_scale.clone()
+    page1 = int(dev.block_table[2, 1])
+    ks[page1, 1, 0] = 255                    # token 65 of request 2: dead, garbage allowed
+    mx.check_metadata("prefill", dev.k_data, ks, dev.block_table, dev.seq_lens, 160, check_scales=True, **args)
 
 
 # ------------------------------------------------------------------ full-size workloads (sampled oracle)
