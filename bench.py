@@ -275,9 +275,9 @@ def main():
         cpu = cpu_baseline(wl, inp, args.cpu_sample)
 
     line = {
-        "metric": "scored (row x head x token) triples/s; us/call, HBM GB/s and scaled-MFMA util alongside",
+        "metric": "\u00b5s/call and scored (row\u00d7head\u00d7token)/s; HBM GB/s + scaled-MFMA util vs peak",
         "value": value,
-        "unit": "(row x head x token)/s",
+        "unit": "(row\u00d7head\u00d7token)/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
