@@ -196,6 +196,30 @@ int mxs_score_decode(const mxs_query* q, const mxs_kcache* k, const mxs_batch* b
 int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
                      const mxs_out* logits, const mxs_out* block_scores, const mxs_plan* plan, void* stream);
 
+/* Top-k page selection over block scores (ATOM #2770, "How it works": the
+ * selection follows the scorer, and the squashed sparse-attention commit: the
+ * tail page is always selected; k, the tie rule and the result order are this
+ * library's reading). For every (row, head) of block_scores [rows, H, NB]
+ * (as written by the scoring calls: -inf for pages holding no visible
+ * token), writes to pages [rows, H, k] (int32, device memory owned by the
+ * caller):
+ *   - the tail page, (limit - 1) / page_size, where limit is the row's
+ *     visible token count (prefill: min(seq_len, prefix_len + i + 1) for the
+ *     request's i-th row; decode: seq_len; both clipped to max_seq_len);
+ *   - the other live pages (finite score) with the largest scores, ties to
+ *     the lower page index, up to k pages in all;
+ *   in ascending page order, then -1 for places left when fewer than k pages
+ *   are live. NB = ceil(max_seq_len / page_size), at most 4096.
+ * mode: MXS_MODE_DECODE (rows are requests; batch->seq_lens used) or
+ * MXS_MODE_PREFILL / MXS_MODE_LOGITS (rows per cu_seqlens_q; seq_lens and
+ * prefix_lens used). batch->block_table is not read and may be NULL.
+ * Strides in elements. Same device contract and asynchrony as the scoring
+ * calls; k = 0 or no rows is a no-op. Returns MXS_OK, MXS_EINVAL,
+ * MXS_ELAYOUT, MXS_EUNSUPPORTED (NB > 4096 or not gfx950) or MXS_EDEVICE. */
+int mxs_select_pages(int32_t mode, const mxs_batch* batch, int32_t num_heads, int32_t page_size,
+                     const float* block_scores, int64_t bs_row_stride, int64_t bs_head_stride, int32_t k,
+                     int32_t* pages, int64_t pages_row_stride, int64_t pages_head_stride, void* stream);
+
 /* Check of the device-side contract that the scoring calls cannot verify
  * without a device-to-host copy (see "Device contract" above). Synchronous:
  * copies the request metadata (and, with check_scales, the scale bytes of

@@ -73,7 +73,7 @@ class Plan(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("mxs_plan_make", "mxs_plan_make_for", "mxs_score_prefill", "mxs_score_decode", "mxs_score_logits",
-           "mxs_check_metadata", "mxs_last_error", "mxs_version")
+           "mxs_select_pages", "mxs_check_metadata", "mxs_last_error", "mxs_version")
 
 
 def library_path() -> str:
@@ -97,6 +97,10 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [P(Query), P(KCache), P(Batch), ctypes.c_float, P(Out), P(Out), P(Plan), ctypes.c_void_p]
             f.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.mxs_select_pages.argtypes = [i32, P(Batch), i32, i32, ctypes.c_void_p, i64, i64, i32, ctypes.c_void_p, i64,
+                                       i64, ctypes.c_void_p]
+        L.mxs_select_pages.restype = ctypes.c_int
         L.mxs_check_metadata.argtypes = [i32, P(KCache), P(Batch), i32, ctypes.c_void_p]
         L.mxs_check_metadata.restype = ctypes.c_int
         L.mxs_last_error.restype = ctypes.c_char_p
@@ -305,3 +309,36 @@ def check_metadata(mode: str, k_data, k_scale, block_table, seq_lens, max_seq_le
     with torch.cuda.device(dev):
         _check(lib().mxs_check_metadata(m, ctypes.byref(kc), ctypes.byref(ba), int(bool(check_scales)),
                                         _stream(dev, stream)))
+
+
+def select_pages(block_scores: torch.Tensor, k: int, seq_lens, max_seq_len: int, page_size: int, cu_seqlens_q=None,
+                 prefix_lens=None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Top-k pages per (row, head) of block scores [rows, H, NB]: the tail page
+    plus the best other live pages (ties to the lower index), ascending, -1
+    padded -> int32 [rows, H, k]. Decode rows (one per request) when
+    cu_seqlens_q is None, else prefill rows."""
+    dev = _same_device(block_scores, seq_lens, cu_seqlens_q, prefix_lens, out)
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 3 or block_scores.stride(2) != 1:
+        raise ValueError("block_scores must be float32 [rows, H, NB] with unit page stride")
+    R, H, NB = block_scores.shape
+    if NB * page_size < max_seq_len:
+        raise ValueError("block_scores is narrower than ceil(max_seq_len / page_size) pages")
+    B = seq_lens.shape[0]
+    if cu_seqlens_q is None:
+        mode = MXS_MODE_DECODE
+        if R != B:
+            raise ValueError("decode selection needs one block-score row per request")
+        ba = Batch(None, 0, 0, None, _int_vec("seq_lens", seq_lens, B), None, B, B, 1, int(max_seq_len))
+    else:
+        mode = MXS_MODE_PREFILL
+        ba = Batch(None, 0, 0, _int_vec("cu_seqlens_q", cu_seqlens_q, B + 1), _int_vec("seq_lens", seq_lens, B),
+                   _int_vec("prefix_lens", prefix_lens, B), B, R, 0, int(max_seq_len))
+    if out is None:
+        out = torch.empty((R, H, k), dtype=torch.int32, device=dev)
+    if out.dtype != torch.int32 or tuple(out.shape) != (R, H, k) or (k > 0 and out.stride(2) != 1):
+        raise ValueError(f"out must be int32 [{R}, {H}, {k}] with unit stride along k")
+    with torch.cuda.device(dev):
+        _check(lib().mxs_select_pages(mode, ctypes.byref(ba), H, page_size, block_scores.data_ptr(),
+                                      block_scores.stride(0), block_scores.stride(1), int(k), out.data_ptr(),
+                                      out.stride(0), out.stride(1), _stream(dev, stream)))
+    return out

@@ -102,6 +102,74 @@ extern "C" {
 
 const char* mxs_last_error(void) { return g_error.c_str(); }
 
+int mxs_select_pages(int32_t mode, const mxs_batch* bt, int32_t num_heads, int32_t page_size,
+                     const float* block_scores, int64_t bs_row_stride, int64_t bs_head_stride, int32_t k,
+                     int32_t* pages, int64_t pages_row_stride, int64_t pages_head_stride, void* stream) {
+  if (!bt) return fail(MXS_EINVAL, "batch descriptor must not be NULL");
+  if (mode != MXS_MODE_PREFILL && mode != MXS_MODE_DECODE && mode != MXS_MODE_LOGITS)
+    return fail(MXS_EINVAL, "unknown mode %d", mode);
+  if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
+  if (num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", num_heads);
+  if (k < 0) return fail(MXS_EINVAL, "k must be >= 0, got %d", k);
+  if (bt->batch < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  const bool decode = mode == MXS_MODE_DECODE;
+  if (!decode && bt->total_rows < 0) return fail(MXS_EINVAL, "total_rows must be >= 0");
+  const int64_t rows = decode ? bt->batch : bt->total_rows;
+  const int64_t NB = ceil_div(bt->max_seq_len, page_size);
+  if (k == 0 || rows == 0 || bt->batch == 0) return MXS_OK;
+  if (NB > mxs::kSelectMaxPages)
+    return fail(MXS_EUNSUPPORTED, "selection holds at most %d pages per row, got %lld", mxs::kSelectMaxPages,
+                (long long)NB);
+  if (!block_scores || !pages) return fail(MXS_EINVAL, "block_scores and pages must not be NULL");
+  if (!aligned(block_scores, 4) || !aligned(pages, 4)) return fail(MXS_ELAYOUT, "buffers must be 4-byte aligned");
+  if (!bt->seq_lens || (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens)))
+    return fail(MXS_EINVAL, "seq_lens (and for prefill cu_seqlens_q, prefix_lens) must not be NULL");
+  auto check_view = [&](const char* name, int64_t rs, int64_t hs, int64_t width) {
+    if (rs < 0 || hs < 0) return fail(MXS_ELAYOUT, "%s strides must be >= 0", name);
+    if (num_heads > 1 && hs < width) return fail(MXS_ELAYOUT, "%s head stride is narrower than its width", name);
+    int64_t row_span, span;
+    if (!mul_add(num_heads - 1, hs, width, &row_span)) return fail(MXS_ELAYOUT, "%s span overflows", name);
+    if (rows > 1 && rs < row_span) return fail(MXS_ELAYOUT, "%s row stride is narrower than one row", name);
+    if (!mul_add(rows - 1, rs, row_span, &span) || span > INT64_MAX / 4)
+      return fail(MXS_ELAYOUT, "%s span overflows", name);
+    return MXS_OK;
+  };
+  int rc = check_view("block_scores", bs_row_stride, bs_head_stride, NB);
+  if (rc) return rc;
+  rc = check_view("pages", pages_row_stride, pages_head_stride, k);
+  if (rc) return rc;
+  int dev;
+  DeviceInfo info;
+  rc = current_device(&dev, &info);
+  if (rc != MXS_OK) return rc;
+  mxs::SArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.bs = block_scores;
+  a.bs_row_stride = bs_row_stride;
+  a.bs_head_stride = bs_head_stride;
+  a.out = pages;
+  a.out_row_stride = pages_row_stride;
+  a.out_head_stride = pages_head_stride;
+  a.cu = decode ? nullptr : bt->cu_seqlens_q;
+  a.seq = bt->seq_lens;
+  a.prefix = decode ? nullptr : bt->prefix_lens;
+  a.decode = decode ? 1 : 0;
+  a.B = bt->batch;
+  a.H = num_heads;
+  a.NB = (int32_t)NB;
+  a.P = page_size;
+  a.k = k;
+  a.max_seq_len = bt->max_seq_len;
+  a.items = rows * num_heads;
+  const int per = (int)ceil_div(NB > 0 ? NB : 1, 64);
+  // one wave per (row, head) while that fills the chip a few times over; beyond, waves loop
+  const int64_t cap = (int64_t)info.cus * 32;
+  const int64_t grid = std::min<int64_t>(ceil_div(a.items, mxs::kWaves), cap);
+  if (mxs::launch_select(per, grid, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(MXS_EDEVICE, "launching the page selection failed: %s", hipGetErrorString(hipGetLastError()));
+  return MXS_OK;
+}
+
 int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, int32_t check_scales, void* stream) {
   if (!k || !bt) return fail(MXS_EINVAL, "cache and batch descriptors must not be NULL");
   if (mode != MXS_MODE_PREFILL && mode != MXS_MODE_DECODE && mode != MXS_MODE_LOGITS)

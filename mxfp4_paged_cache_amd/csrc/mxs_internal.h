@@ -65,7 +65,30 @@ struct KArgs {
   int32_t vec_lg;           // logit rows 16-byte aligned
 };
 
+// Arguments of the page-selection kernel (mxs_select.hip).
+struct SArgs {
+  const float* bs;          // block scores [rows, H, NB]
+  int64_t bs_row_stride;    // elements
+  int64_t bs_head_stride;
+  int32_t* out;             // selected pages [rows, H, k]
+  int64_t out_row_stride;   // elements
+  int64_t out_head_stride;
+  const int32_t* cu;        // prefill rows: cu_seqlens_q, seq_lens, prefix_lens
+  const int32_t* seq;
+  const int32_t* prefix;
+  int32_t decode;           // 1: row b is request b, its limit is seq_lens[b]
+  int32_t B;
+  int32_t H;
+  int32_t NB;
+  int32_t P;
+  int32_t k;
+  int32_t max_seq_len;
+  int64_t items;            // rows * H
+};
+constexpr int kSelectMaxPages = 64 * 64;   // scores per (row, head) the selection kernel holds (64 per lane)
+
 // Launchers. Return the HIP status of the launch.
+hipError_t launch_select(int per, int64_t grid, const SArgs& a, hipStream_t stream);
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream);

@@ -200,6 +200,23 @@ def test_check_metadata_rejections_before_any_copy(L):
     assert b"NULL" in L.mxs_last_error()
 
 
+def test_select_pages_rejections_before_device_work(L):
+    q, k, b, bs, lg = valid_args()
+    sel = lambda mode, bt, H, P, kk, rs=64 * 8, hs=8, prs=64 * 4, phs=4: L.mxs_select_pages(
+        mode, ctypes.byref(bt) if bt is not None else None, H, P, FAKE, rs, hs, kk, FAKE + 0x10000, prs, phs, None)
+    assert sel(mx.MXS_MODE_PREFILL, None, 64, 128, 4) == mx.MXS_EINVAL
+    assert sel(7, b, 64, 128, 4) == mx.MXS_EINVAL
+    assert sel(mx.MXS_MODE_PREFILL, b, 64, 96, 4) == mx.MXS_ELAYOUT
+    assert sel(mx.MXS_MODE_PREFILL, b, 0, 128, 4) == mx.MXS_EINVAL
+    assert sel(mx.MXS_MODE_PREFILL, b, 64, 128, -1) == mx.MXS_EINVAL
+    assert sel(mx.MXS_MODE_PREFILL, b, 64, 128, 0) == mx.MXS_OK                      # nothing to write
+    assert sel(mx.MXS_MODE_PREFILL, b, 64, 128, 4, hs=4) == mx.MXS_ELAYOUT            # narrow score rows
+    assert sel(mx.MXS_MODE_PREFILL, b, 64, 128, 4, phs=2) == mx.MXS_ELAYOUT           # narrow output rows
+    wide = mx.Batch.from_buffer_copy(bytes(b))
+    wide.max_seq_len = 128 * 4097
+    assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4, rs=64 * 4097, hs=4097) == mx.MXS_EUNSUPPORTED
+
+
 def test_python_layer_rejects_cpu_tensors():
     import torch
     q = torch.zeros((1, 1, 128), dtype=torch.bfloat16)

@@ -1,0 +1,102 @@
+"""GPU parity of the top-k page selection (mxs_select_pages, through the C ABI)
+against the CPU definition in oracle/topk.py: page indices bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_paged_cache_amd as mx
+from mxfp4_paged_cache_amd import workloads as W
+from oracle import topk
+from tests.gpu_helpers import gpu_inputs, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def synthetic_scores(rng, limits, H, P, NB, n_values=5):
+    """Scores from a few values (many ties); -inf past each row's limit and on
+    some pages before it, as the scorer would write for dead pages."""
+    vals = np.linspace(-3, 3, n_values).astype(np.float32)
+    R = len(limits)
+    s = vals[rng.integers(0, n_values, (R, H, NB))]
+    s[rng.random((R, H, NB)) < 0.1] = -np.inf
+    for r in range(R):
+        live = -(-int(limits[r]) // P)
+        s[r, :, live:] = -np.inf
+        if limits[r] > 0:
+            s[r, :, (int(limits[r]) - 1) // P] = vals[rng.integers(0, n_values)]
+    return s
+
+
+@pytest.mark.parametrize("k", [1, 4, 13, 40])
+@pytest.mark.parametrize("NB", [9, 64, 100, 700, 2100, 4096])
+def test_prefill_rows_match_oracle(NB, k):
+    P = 64
+    rng = np.random.default_rng(NB * 7 + k)
+    q_lens, prefix = [3, 0, 6, 1], [NB * P // 2, 5, NB * P - 6, 0]
+    seq = [min(p + q, NB * P) for p, q in zip(prefix, q_lens)]
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    msl = NB * P
+    lim = topk.row_limits("prefill", seq, msl, cu, prefix)
+    s = synthetic_scores(rng, lim, 3, P, NB)
+    say(f"prefill select NB={NB} k={k} rows={len(lim)}")
+    got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P,
+                          cu_seqlens_q=torch.from_numpy(cu).cuda(),
+                          prefix_lens=torch.tensor(prefix, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
+
+
+@pytest.mark.parametrize("P", [64, 128])
+def test_decode_rows_and_strided_views(P):
+    rng = np.random.default_rng(P)
+    seq = [0, 1, P, P + 1, 30 * P, 31 * P - 3]
+    msl = 31 * P
+    NB = 31
+    lim = topk.row_limits("decode", seq, msl)
+    s = synthetic_scores(rng, lim, 5, P, NB, n_values=3)
+    big = torch.full((len(seq), 5, NB + 7), 7.0, device="cuda")        # padded rows: strided input view
+    big[:, :, :NB] = torch.from_numpy(s).cuda()
+    outv = torch.full((len(seq), 5, 16), -7, dtype=torch.int32, device="cuda")[:, :, :6]   # strided output view
+    got = mx.select_pages(big[:, :, :NB], 6, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P, out=outv)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, 6))
+
+
+def test_selection_of_scorer_output():
+    # the step as it follows the scorer: block scores of the 64-row prefill
+    # workload (ctx 1024, 8 pages), k = 3
+    wl = W.prefill_small()
+    host = W.make_inputs(wl, 21, "cpu")
+    dev = gpu_inputs(host)
+    bs, _ = run_gpu(dev, want_logits=False)
+    got = mx.select_pages(bs, 3, dev.seq_lens, wl.window, wl.page_size, cu_seqlens_q=dev.cu_seqlens_q,
+                          prefix_lens=dev.prefix_lens)
+    torch.cuda.synchronize()
+    lim = topk.row_limits("prefill", wl.seq_lens, wl.window, host.cu_seqlens_q.numpy(), wl.prefix_lens)
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(bs.cpu().numpy(), lim, wl.page_size, 3))
+
+
+def test_full_size_selection_sampled_rows():
+    # block scores of the 4096-row, 128K-context prefill (4096 x 64 x 1024),
+    # k = 64; 12 sampled rows (all heads) against the oracle
+    wl = W.prefill_long()
+    dev = W.make_inputs(wl, 22, "cuda")
+    bs, _ = run_gpu(dev, want_logits=False)
+    got = mx.select_pages(bs, 64, dev.seq_lens, wl.window, wl.page_size, cu_seqlens_q=dev.cu_seqlens_q,
+                          prefix_lens=dev.prefix_lens)
+    torch.cuda.synchronize()
+    lim = topk.row_limits("prefill", wl.seq_lens, wl.window, dev.cu_seqlens_q.cpu().numpy(), wl.prefix_lens)
+    rows = np.array([0, 1, 777, 2048, 4094, 4095] + list(np.random.default_rng(3).integers(0, 4096, 6)))
+    ref = topk.select_pages(bs[rows].cpu().numpy(), lim[rows], wl.page_size, 64)
+    assert np.array_equal(got[rows].cpu().numpy(), ref)
+    # every selection holds its row's tail page
+    tails = (torch.from_numpy(lim).cuda() - 1) // wl.page_size
+    assert bool((got == tails[:, None, None]).any(dim=2).all())
