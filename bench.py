@@ -27,7 +27,8 @@ the roofline picks up while the kernel sources still hash the same.
 
 --config selects another workload (1: prefill 64 rows ctx 1k with logits,
 3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
-5: logits, 64-token pages in a shared pool past 4.608e9 bytes).
+5: logits, 64-token pages in a shared pool past 4.608e9 bytes, 6: top-64 page
+selection over the block scores of config 3).
 """
 from __future__ import annotations
 
@@ -57,8 +58,10 @@ def log(*a):
 
 
 def kernel_name(wl) -> str:
-    """The kernel a workload runs: decode, the block-score kernel, or the logits
-    kernel (every call that writes logits)."""
+    """The kernel a workload runs: decode, the block-score kernel, the logits
+    kernel (every call that writes logits) or the page selection."""
+    if wl.select_k:
+        return "k_select"
     if wl.mode == "decode":
         return "k_decode"
     return "k_logits" if (wl.mode == "logits" or wl.want_logits) else "k_prefill"
@@ -92,8 +95,8 @@ def pmc_summary(dbs):
         per = {}
         for name, disp, val, kname in con.execute(
                 "select counter_name, dispatch_id, value, kernel_name from counters_collection"):
-            kind = "copy" if "neg" in kname else next((k for k in ("k_decode", "k_prefill", "k_logits") if k in kname),
-                                                      None)
+            kind = "copy" if "neg" in kname else next(
+                (k for k in ("k_decode", "k_prefill", "k_logits", "k_select") if k in kname), None)
             if kind is None:
                 continue
             per.setdefault((name, kind), {}).setdefault(disp, 0.0)
@@ -103,7 +106,7 @@ def pmc_summary(dbs):
     out = {}
     for counter, field in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         copy = acc.get((counter, "copy"))
-        for k in ("k_decode", "k_prefill", "k_logits"):
+        for k in ("k_decode", "k_prefill", "k_logits", "k_select"):
             v = acc.get((counter, k))
             if v is None or not copy:
                 continue
@@ -117,6 +120,9 @@ def algorithmic_bytes(wl, inp) -> int:
     """Bytes a call must move at minimum: every live page once (data + scales),
     the query rows, the block-table entries of live pages, and every output
     element written once."""
+    if wl.select_k:
+        # the selection reads every block score and writes k page ids per (row, head)
+        return wl.T * wl.H * (wl.NB + wl.select_k) * 4 + (wl.B * 3 + 1) * 4
     P = wl.page_size
     pages = sum((min(s, wl.window) + P - 1) // P for s in wl.seq_lens)
     kbytes = pages * P * 68
@@ -194,9 +200,19 @@ def main():
     plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks)
     log(f"plan: {plan.as_dict()}")
 
+    sel = None
+    if wl.select_k:
+        # the selection's input: this prefill's block scores, computed once before timing
+        mx.score_prefill(inp.q, inp.k_data, inp.k_scale, inp.block_tables[0], inp.cu_seqlens_q, inp.seq_lens,
+                         inp.prefix_lens, max(wl.q_lens), Wd, S, out=bs, plan=plan)
+        sel = torch.empty((T, H, wl.select_k), dtype=torch.int32, device=dev)
+
     def call(i):
         bt = inp.block_tables[i % len(inp.block_tables)]
-        if wl.mode == "decode":
+        if wl.select_k:
+            mx.select_pages(bs, wl.select_k, inp.seq_lens, Wd, P, cu_seqlens_q=inp.cu_seqlens_q,
+                            prefix_lens=inp.prefix_lens, out=sel)
+        elif wl.mode == "decode":
             mx.score_decode(inp.q, inp.k_data, inp.k_scale, bt, inp.seq_lens, Wd, S, out=bs,
                             logits=lg if lg is not None else False, plan=plan)
         elif wl.mode == "logits":
@@ -249,12 +265,14 @@ def main():
     ms = ms_total / args.steps   # one kernel launch per step: this is the launch's average duration
 
     triples = wl.live_triples()
-    value = triples / (ms / 1e3)
+    # throughput: scored (row, head, token) triples/s; the selection consumes (row, head, page) block scores
+    units = wl.T * wl.H * wl.NB if wl.select_k else triples
+    value = units / (ms / 1e3)
     abytes = algorithmic_bytes(wl, inp)
     flops = 2.0 * 128 * triples
     gbps = abytes / (ms / 1e3) / 1e9
     tflops = flops / (ms / 1e3) / 1e12
-    hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64)
+    hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k)
     traffic = None
     tpath = args.traffic or traffic_path(wl)
     if os.path.exists(tpath):
@@ -272,12 +290,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, args.cpu_sample)
+        cpu = cpu_baseline_select(wl, bs, inp, args.cpu_sample) if wl.select_k else cpu_baseline(wl, inp, args.cpu_sample)
 
     line = {
         "metric": "\u00b5s/call and scored (row\u00d7head\u00d7token)/s; HBM GB/s + scaled-MFMA util vs peak",
         "value": value,
-        "unit": "(row\u00d7head\u00d7token)/s",
+        "unit": "(row\u00d7head\u00d7page)/s" if wl.select_k else "(row\u00d7head\u00d7token)/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -291,12 +309,13 @@ def main():
         "config": {"workload": wl.name, "batch": wl.B, "query_rows": T, "heads": H, "head_dim": 128,
                    "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype,
                    "e8m0_range": [wl.scale_lo, wl.scale_hi], "outputs": ("block_scores" if wl.want_blocks else "") +
-                   ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables)},
+                   ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables),
+                   **({"select_k": wl.select_k} if wl.select_k else {})},
         "hbm_gbps": round(gbps, 1),
-        "mfma_tflops": round(tflops, 2),
-        "mfma_util_fp8_rate": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+        "mfma_tflops": None if wl.select_k else round(tflops, 2),
+        "mfma_util_fp8_rate": None if wl.select_k else round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
         "algorithmic_bytes": abytes,
-        "live_triples": triples,
+        "live_triples": None if wl.select_k else triples,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
@@ -304,6 +323,24 @@ def main():
         "kernel": kernel_name(wl),
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_select(wl, bs, inp, sample_rows: int):
+    """The selection oracle (test infrastructure, pure Python, one core) on a
+    bounded sample of rows; reported as (row, head, page) scores/s."""
+    import numpy as np
+    from oracle import topk
+    # ~5 s of the pure-Python oracle (about 4.5e6 scores/s on one core)
+    n_rows = sample_rows or max(1, int(5 * 4.5e6) // (wl.H * wl.NB))
+    rows = np.sort(np.random.default_rng(1234).choice(wl.T, size=min(n_rows, wl.T), replace=False))
+    lim = topk.row_limits("prefill", wl.seq_lens, wl.window, inp.cu_seqlens_q.cpu().numpy(), wl.prefix_lens)
+    scores = bs[rows].cpu().numpy()
+    t0 = time.perf_counter()
+    topk.select_pages(scores, lim[rows], wl.page_size, wl.select_k)
+    dt = time.perf_counter() - t0
+    n = len(rows) * wl.H * wl.NB
+    return {"value": n / dt, "unit": "(row\u00d7head\u00d7page)/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.T} rows, all heads and pages ({n} block scores), {dt:.2f} s"}
 
 
 def cpu_baseline(wl, inp, sample_rows: int):
@@ -349,7 +386,7 @@ def cpu_baseline(wl, inp, sample_rows: int):
                  cu_seqlens_q=cu, prefix_lens=inp.prefix_lens.cpu().numpy(), rows=rows,
                  want_logits=wl.want_logits, want_blocks=wl.want_blocks, num_threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": sample_triples / dt, "unit": "(row x head x token)/s", "cores": threads, "kind": "oracle",
+    return {"value": sample_triples / dt, "unit": "(row\u00d7head\u00d7token)/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {T} query rows ({sample_triples} live triples, all heads and pages of "
                       f"those rows), {dt:.2f} s"}
 

@@ -18,9 +18,16 @@ using namespace dev;
 //
 // Scores become order-preserving unsigned keys; pages without a visible token
 // (-inf) get key 0 and the tail page the largest key, so it is always chosen.
-// A bitwise search over the key finds T, the k-th largest key among the live
-// pages (k clipped to their count); the result is every page with key > T and
-// the lowest-indexed pages with key == T, emitted in page order.
+// The result is every page whose key exceeds T, the k-th largest key (k
+// clipped to the live pages), and the lowest-indexed pages whose key equals
+// T, emitted in page order. T comes from a greedy bitwise search:
+//   * pruning: if each of n lanes holds j keys >= some x, then n j keys are
+//     >= x; with x the smallest such j-th lane key (j = 2 or 1) and k <= n j,
+//     T >= x, so only keys >= x are candidates; they are compacted in page
+//     order into LDS and searched with as few registers per lane as they need;
+//   * every candidate but the tail lies in [x, K] (K the largest non-tail
+//     key), so T shares the leading bits x and K have in common and only the
+//     bits below them are searched.
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t b = __float_as_uint(s);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -28,12 +35,110 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 __device__ __forceinline__ uint32_t ballot_count(bool p) { return __builtin_popcountll(__ballot(p)); }
 
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, d));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, d));
+  return x;
+}
+
+// The scores of one (row, head), all loads issued together (indices past NB
+// read the last page's score and are then dropped, so no load is predicated).
+template <int PER>
+__device__ __forceinline__ void load_scores(const SArgs& a, int64_t item, int lane, float (&v)[PER]) {
+  const int64_t r = item / a.H;
+  const int h = (int)(item - r * a.H);
+  const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) v[m] = srow[min(64 * m + lane, a.NB - 1)];
+}
+
+// Greedy search for the largest T with count(keys >= T) >= keff, over the
+// bits below the first nbits; T starts from those leading bits.
+template <int N>
+__device__ __forceinline__ uint32_t search_threshold(const uint32_t (&k)[N], uint32_t T, int nbits, uint32_t keff) {
+  for (int bit = nbits - 1; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < N; ++q) cnt += ballot_count(k[q] >= cand);
+    if (cnt >= keff) T = cand;
+  }
+  return T;
+}
+
+// Emit, in page order, the keys above T and the first need_eq keys equal to
+// T: page ids go to sel[] (LDS) while k fits, else straight to the output row.
+template <int N>
+__device__ __forceinline__ uint32_t emit(const uint32_t (&k)[N], const int32_t (&idx)[N], uint32_t T, uint32_t need_eq,
+                                         int32_t* sel, int32_t* orow) {
+  uint32_t written = 0, eq_seen = 0;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const bool eq = k[q] == T;
+    const uint64_t beq = __ballot(eq);
+    const bool take = k[q] > T || (eq && eq_seen + lanes_below(beq) < need_eq);
+    const uint64_t bt = __ballot(take);
+    if (take) (sel ? sel : orow)[written + lanes_below(bt)] = idx[q];
+    written += __builtin_popcountll(bt);
+    eq_seen += __builtin_popcountll(beq);
+  }
+  return written;
+}
+
+constexpr int kSelectCand = 512;   // candidates per (row, head) the pruned search holds (8 per lane)
+
+// Search and emit over the ncand candidates compacted in LDS (page order),
+// NC per lane: candidate 64 q + lane.
+template <int NC>
+__device__ __forceinline__ uint32_t select_candidates(const uint32_t* ck, const int32_t* ci, uint32_t ncand, int lane,
+                                                      uint32_t T0, int nbits, uint32_t keff, int32_t* sel,
+                                                      int32_t* orow) {
+  uint32_t k2[NC];
+  int32_t i2[NC];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const uint32_t c = 64 * q + lane;
+    k2[q] = c < ncand ? ck[c] : 0u;
+    i2[q] = c < ncand ? ci[c] : 0;
+  }
+  const uint32_t T = search_threshold(k2, T0, nbits, keff);
+  uint32_t gt = 0;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) gt += ballot_count(k2[q] > T);
+  return emit(k2, i2, T, keff - gt, sel, orow);
+}
+constexpr int kSelectStage = 256;  // results staged in LDS for one coalesced store when k fits
+
 template <int PER>
 __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
+  __shared__ uint32_t cand_keys[kWaves][kSelectCand];
+  __shared__ int32_t cand_idx[kWaves][kSelectCand];
+  __shared__ int32_t sel_all[kWaves][kSelectStage];
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + wv;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
+  uint32_t* ck = cand_keys[wv];
+  int32_t* ci = cand_idx[wv];
+  int32_t* sel = a.k <= kSelectStage ? sel_all[wv] : nullptr;
+  // the next item's scores are in flight while this one is selected
+  float nxt[PER];
+  if (wave < a.items) load_scores<PER>(a, wave, lane, nxt);
   for (int64_t item = wave; item < a.items; item += nw) {
+    float cur[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) cur[m] = nxt[m];
+    if (item + nw < a.items) load_scores<PER>(a, item + nw, lane, nxt);
     const int64_t r = item / a.H;
     const int h = (int)(item - r * a.H);
     // the row's visible tokens, as the scorer masks them
@@ -51,51 +156,89 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
     lim = clampi(lim, 0, a.max_seq_len);
     const int tail = lim > 0 ? (lim - 1) / a.P : -1;
 
-    const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
     uint32_t key[PER];
+    int32_t idx[PER];
+    uint32_t t1 = 0, t2 = 0, kmax = 0;   // the lane's two largest keys; its largest non-tail key
+    bool tail_here = false;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
       const int j = 64 * m + lane;
-      const float s = j < a.NB ? srow[j] : kNegInf;
-      key[m] = (s - s == 0.0f) ? (j == tail ? 0xFFFFFFFFu : order_key(s)) : 0u;   // finite test
+      idx[m] = j;
+      const uint32_t bits = __float_as_uint(cur[m]);
+      const bool live = j < a.NB && (bits & 0x7F800000u) != 0x7F800000u;   // finite score
+      const bool is_tail = live && j == tail;
+      tail_here |= is_tail;
+      key[m] = live ? (is_tail ? 0xFFFFFFFFu : order_key(cur[m])) : 0u;
+      if (!is_tail) kmax = max(kmax, key[m]);
+      t2 = max(t2, min(t1, key[m]));
+      t1 = max(t1, key[m]);
     }
     uint32_t live = 0;
 #pragma unroll
     for (int m = 0; m < PER; ++m) live += ballot_count(key[m] != 0u);
     const uint32_t keff = min((uint32_t)a.k, live);
+    const bool tail_live = __ballot(tail_here) != 0;
 
     int32_t* orow = a.out + r * a.out_row_stride + (int64_t)h * a.out_head_stride;
     uint32_t written = 0;
     if (keff > 0) {
-      uint32_t T = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        uint32_t cnt = 0;
+      if (tail_live && keff == 1) {
+        // only the tail page
+        if (sel) { if (lane == 0) sel[0] = tail; } else if (lane == 0) orow[0] = tail;
+        written = 1;
+      } else {
+        // lower bound x of T: the smallest second-largest or largest lane key
+        // (valid when keff <= 2 n2 or <= n1 lanes hold one), else none
+        const uint32_t n1 = ballot_count(t1 != 0u), n2 = ballot_count(t2 != 0u);
+        const uint32_t x2 = wave_min(t2 != 0u ? t2 : 0xFFFFFFFFu);
+        const uint32_t x1 = wave_min(t1 != 0u ? t1 : 0xFFFFFFFFu);
+        const uint32_t x = keff <= 2 * n2 ? x2 : (keff <= n1 ? x1 : 1u);
+        const uint32_t K = wave_max(kmax);
+        const uint32_t diff = x ^ K;
+        const int nbits = diff ? 32 - __builtin_clz(diff) : 0;
+        const uint32_t T0 = nbits == 32 ? 0u : (x & ~((1u << nbits) - 1u));
+        uint32_t ncand = 0;
 #pragma unroll
-        for (int m = 0; m < PER; ++m) cnt += ballot_count(key[m] >= cand);
-        if (cnt >= keff) T = cand;
-      }
-      uint32_t gt = 0;
+        for (int m = 0; m < PER; ++m) ncand += ballot_count(key[m] >= x);
+        if (PER > kSelectCand / 64 && ncand <= (uint32_t)kSelectCand) {
+          uint32_t at = 0;
 #pragma unroll
-      for (int m = 0; m < PER; ++m) gt += ballot_count(key[m] > T);
-      const uint32_t need_eq = keff - gt;
-      uint32_t eq_seen = 0;
+          for (int m = 0; m < PER; ++m) {
+            const bool c = key[m] >= x;
+            const uint64_t bc = __ballot(c);
+            if (c) {
+              ck[at + lanes_below(bc)] = key[m];
+              ci[at + lanes_below(bc)] = idx[m];
+            }
+            at += __builtin_popcountll(bc);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // the candidates back in registers, as few per lane as they need
+          if (ncand <= 128)
+            written = select_candidates<2>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+          else if (ncand <= 256)
+            written = select_candidates<4>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+          else
+            written = select_candidates<8>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+        } else {
+          const uint32_t T = search_threshold(key, T0, nbits, keff);
+          uint32_t gt = 0;
 #pragma unroll
-      for (int m = 0; m < PER; ++m) {
-        const bool eq = key[m] == T;
-        const uint64_t beq = __ballot(eq);
-        const uint32_t eq_rank = eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(beq >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)beq, 0u));
-        const bool sel = key[m] > T || (eq && eq_rank < need_eq);
-        const uint64_t bsel = __ballot(sel);
-        const uint32_t pos = written + __builtin_amdgcn_mbcnt_hi((uint32_t)(bsel >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bsel, 0u));
-        if (sel) orow[pos] = 64 * m + lane;
-        written += __builtin_popcountll(bsel);
-        eq_seen += __builtin_popcountll(beq);
+          for (int m = 0; m < PER; ++m) gt += ballot_count(key[m] > T);
+          written = emit(key, idx, T, keff - gt, sel, orow);
+        }
       }
     }
-    for (uint32_t p = written + lane; p < (uint32_t)a.k; p += 64) orow[p] = -1;
+    if (sel) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int p = lane; p < a.k; p += 64) orow[p] = (uint32_t)p < written ? sel[p] : -1;
+    } else {
+      for (uint32_t p = written + lane; p < (uint32_t)a.k; p += 64) orow[p] = -1;
+    }
   }
 }
 

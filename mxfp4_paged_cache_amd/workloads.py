@@ -55,6 +55,7 @@ class Workload:
     table_fill: str = "pad"         # entries past a request's pages: "pad" (-1) or "perm" (more distinct pages)
     max_seq_len: Optional[int] = None
     tables: int = 1                 # disjoint block tables (benchmark rotation)
+    select_k: int = 0               # > 0: the workload is top-k page selection over this prefill's block scores
     note: str = ""
 
     @property
@@ -235,10 +236,19 @@ def logits_shared_pool() -> Workload:
                     layout="shared", shared_first_page=529_412, table_pad=8)
 
 
+def select_after_prefill_long() -> Workload:
+    """Top-64 page selection over the block scores of the 4096-row, 128K-context prefill (4096 x 64 x 1024)."""
+    wl = prefill_long()
+    wl.name = "select_k64_q4096_ctx128k"
+    wl.select_k = 64
+    return wl
+
+
 CONFIGS = {
     1: prefill_small,
     2: decode_b64_128k,
     3: prefill_long,
     4: prefill_chunk,
     5: logits_shared_pool,
+    6: select_after_prefill_long,
 }
