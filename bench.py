@@ -28,7 +28,8 @@ the roofline picks up while the kernel sources still hash the same.
 --config selects another workload (1: prefill 64 rows ctx 1k with logits,
 3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
 5: logits, 64-token pages in a shared pool past 4.608e9 bytes, 6: top-64 page
-selection over the block scores of config 3).
+selection over the block scores of config 3, 7: writing 2^20 bf16 keys into
+MXFP4 page slots).
 """
 from __future__ import annotations
 
@@ -62,6 +63,8 @@ def kernel_name(wl) -> str:
     kernel (every call that writes logits) or the page selection."""
     if wl.select_k:
         return "k_select"
+    if wl.write_tokens:
+        return "k_write"
     if wl.mode == "decode":
         return "k_decode"
     return "k_logits" if (wl.mode == "logits" or wl.want_logits) else "k_prefill"
@@ -96,7 +99,7 @@ def pmc_summary(dbs):
         for name, disp, val, kname in con.execute(
                 "select counter_name, dispatch_id, value, kernel_name from counters_collection"):
             kind = "copy" if "neg" in kname else next(
-                (k for k in ("k_decode", "k_prefill", "k_logits", "k_select") if k in kname), None)
+                (k for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write") if k in kname), None)
             if kind is None:
                 continue
             per.setdefault((name, kind), {}).setdefault(disp, 0.0)
@@ -106,7 +109,7 @@ def pmc_summary(dbs):
     out = {}
     for counter, field in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         copy = acc.get((counter, "copy"))
-        for k in ("k_decode", "k_prefill", "k_logits", "k_select"):
+        for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write"):
             v = acc.get((counter, k))
             if v is None or not copy:
                 continue
@@ -120,6 +123,9 @@ def algorithmic_bytes(wl, inp) -> int:
     """Bytes a call must move at minimum: every live page once (data + scales),
     the query rows, the block-table entries of live pages, and every output
     element written once."""
+    if wl.write_tokens:
+        # the writer reads each bf16 key (256 B) and its slot (8 B) and writes 64 + 4 B
+        return wl.write_tokens * (256 + 8 + 68)
     if wl.select_k:
         # the selection reads every block score and writes k page ids per (row, head)
         return wl.T * wl.H * (wl.NB + wl.select_k) * 4 + (wl.B * 3 + 1) * 4
@@ -207,9 +213,21 @@ def main():
                          inp.prefix_lens, max(wl.q_lens), Wd, S, out=bs, plan=plan)
         sel = torch.empty((T, H, wl.select_k), dtype=torch.int32, device=dev)
 
+    wk = wslots = None
+    if wl.write_tokens:
+        # keys N(0,1) in bf16; whole pages in a seeded random page order
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed * 1000003 + 77)
+        wk = torch.randn((wl.write_tokens, 128), generator=g, device=dev).to(torch.bfloat16)
+        npages = wl.write_tokens // P
+        pages = torch.randperm(wl.pool_pages, generator=g, device=dev)[:npages]
+        wslots = (pages[:, None] * P + torch.arange(P, device=dev)[None, :]).reshape(-1).to(torch.int64)
+
     def call(i):
         bt = inp.block_tables[i % len(inp.block_tables)]
-        if wl.select_k:
+        if wl.write_tokens:
+            mx.write_pages(wk, wslots, inp.k_data, inp.k_scale)
+        elif wl.select_k:
             mx.select_pages(bs, wl.select_k, inp.seq_lens, Wd, P, cu_seqlens_q=inp.cu_seqlens_q,
                             prefix_lens=inp.prefix_lens, out=sel)
         elif wl.mode == "decode":
@@ -266,13 +284,14 @@ def main():
 
     triples = wl.live_triples()
     # throughput: scored (row, head, token) triples/s; the selection consumes (row, head, page) block scores
-    units = wl.T * wl.H * wl.NB if wl.select_k else triples
+    units = wl.write_tokens if wl.write_tokens else (wl.T * wl.H * wl.NB if wl.select_k else triples)
     value = units / (ms / 1e3)
     abytes = algorithmic_bytes(wl, inp)
     flops = 2.0 * 128 * triples
     gbps = abytes / (ms / 1e3) / 1e9
     tflops = flops / (ms / 1e3) / 1e12
-    hbm_bound = wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k)
+    hbm_bound = (wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k) or
+                 bool(wl.write_tokens))
     traffic = None
     tpath = args.traffic or traffic_path(wl)
     if os.path.exists(tpath):
@@ -290,12 +309,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_select(wl, bs, inp, args.cpu_sample) if wl.select_k else cpu_baseline(wl, inp, args.cpu_sample)
+        if wl.write_tokens:
+            cpu = cpu_baseline_write(wl, wk, wslots, args.cpu_sample)
+        elif wl.select_k:
+            cpu = cpu_baseline_select(wl, bs, inp, args.cpu_sample)
+        else:
+            cpu = cpu_baseline(wl, inp, args.cpu_sample)
 
     line = {
         "metric": "\u00b5s/call and scored (row\u00d7head\u00d7token)/s; HBM GB/s + scaled-MFMA util vs peak",
         "value": value,
-        "unit": "(row\u00d7head\u00d7page)/s" if wl.select_k else "(row\u00d7head\u00d7token)/s",
+        "unit": "tokens/s" if wl.write_tokens else (
+            "(row\u00d7head\u00d7page)/s" if wl.select_k else "(row\u00d7head\u00d7token)/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -310,12 +335,13 @@ def main():
                    "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype,
                    "e8m0_range": [wl.scale_lo, wl.scale_hi], "outputs": ("block_scores" if wl.want_blocks else "") +
                    ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables),
-                   **({"select_k": wl.select_k} if wl.select_k else {})},
+                   **({"select_k": wl.select_k} if wl.select_k else {}),
+                   **({"write_tokens": wl.write_tokens} if wl.write_tokens else {})},
         "hbm_gbps": round(gbps, 1),
-        "mfma_tflops": None if wl.select_k else round(tflops, 2),
-        "mfma_util_fp8_rate": None if wl.select_k else round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+        "mfma_tflops": None if (wl.select_k or wl.write_tokens) else round(tflops, 2),
+        "mfma_util_fp8_rate": None if (wl.select_k or wl.write_tokens) else round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
         "algorithmic_bytes": abytes,
-        "live_triples": None if wl.select_k else triples,
+        "live_triples": None if (wl.select_k or wl.write_tokens) else triples,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
@@ -323,6 +349,24 @@ def main():
         "kernel": kernel_name(wl),
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_write(wl, wk, wslots, sample_tokens: int):
+    """The writer oracle (test infrastructure, pure Python, one core) on a
+    bounded sample of the keys; reported as tokens/s."""
+    import numpy as np
+    import torch
+    from oracle import writer
+    n = sample_tokens or 8192
+    bits = wk[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+    P = wl.page_size
+    kd = np.zeros((n // P + 1, P, 64), np.uint8)
+    ks = np.zeros((n // P + 1, P, 4), np.uint8)
+    t0 = time.perf_counter()
+    writer.write_pages(bits, np.arange(n), kd, ks, P)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.write_tokens} keys, {dt:.2f} s"}
 
 
 def cpu_baseline_select(wl, bs, inp, sample_rows: int):

@@ -196,6 +196,24 @@ int mxs_score_decode(const mxs_query* q, const mxs_kcache* k, const mxs_batch* b
 int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* batch, float sm_scale,
                      const mxs_out* logits, const mxs_out* block_scores, const mxs_plan* plan, void* stream);
 
+/* MXFP4 index-K writer (ATOM #2770, "Summary" and the write-path commit:
+ * the index key is quantized straight into its pool page slot; the pages give
+ * no conversion rule, this library uses the OCP Microscaling v1.0 one for FP4
+ * E2M1 with an E8M0 scale per 32 elements). Token t of k (bf16 [num_tokens,
+ * 128], head_dim contiguous, row stride in elements, 16-byte aligned rows)
+ * goes to slot slot_mapping[t] = page * page_size + offset (int64; -1, or a
+ * page past cache->num_pages, skips the token): for each 32-element block,
+ * e = floor(log2(amax)) - 2 is stored as the e8m0 byte e + 127 clipped to
+ * [1, 254], and each element as the e2m1 code nearest to x / 2^e (ties to the
+ * even code, saturated at 6, sign kept), element 2m in the low nibble of
+ * data byte m. Writes 64 data bytes and 4 scale bytes per token into the
+ * cache views and nothing else. Non-finite keys are outside the contract.
+ * Two tokens with the same slot race. Asynchronous on stream; num_tokens = 0
+ * is a no-op. Returns MXS_OK, MXS_EINVAL, MXS_ELAYOUT, MXS_EUNSUPPORTED or
+ * MXS_EDEVICE. */
+int mxs_write_pages(const void* k, int64_t k_row_stride, int64_t num_tokens, const int64_t* slot_mapping,
+                    const mxs_kcache* cache, void* stream);
+
 /* Top-k page selection over block scores (ATOM #2770, "How it works": the
  * selection follows the scorer, and the squashed sparse-attention commit: the
  * tail page is always selected; k, the tie rule and the result order are this

@@ -73,7 +73,7 @@ class Plan(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("mxs_plan_make", "mxs_plan_make_for", "mxs_score_prefill", "mxs_score_decode", "mxs_score_logits",
-           "mxs_select_pages", "mxs_check_metadata", "mxs_last_error", "mxs_version")
+           "mxs_write_pages", "mxs_select_pages", "mxs_check_metadata", "mxs_last_error", "mxs_version")
 
 
 def library_path() -> str:
@@ -101,6 +101,8 @@ def lib():
         L.mxs_select_pages.argtypes = [i32, P(Batch), i32, i32, ctypes.c_void_p, i64, i64, i32, ctypes.c_void_p, i64,
                                        i64, ctypes.c_void_p]
         L.mxs_select_pages.restype = ctypes.c_int
+        L.mxs_write_pages.argtypes = [ctypes.c_void_p, i64, i64, ctypes.c_void_p, P(KCache), ctypes.c_void_p]
+        L.mxs_write_pages.restype = ctypes.c_int
         L.mxs_check_metadata.argtypes = [i32, P(KCache), P(Batch), i32, ctypes.c_void_p]
         L.mxs_check_metadata.restype = ctypes.c_int
         L.mxs_last_error.restype = ctypes.c_char_p
@@ -342,3 +344,20 @@ def select_pages(block_scores: torch.Tensor, k: int, seq_lens, max_seq_len: int,
                                       block_scores.stride(0), block_scores.stride(1), int(k), out.data_ptr(),
                                       out.stride(0), out.stride(1), _stream(dev, stream)))
     return out
+
+
+def write_pages(k: torch.Tensor, slot_mapping: torch.Tensor, k_data, k_scale, stream=None) -> None:
+    """Quantize bf16 keys k [N, 128] into MXFP4 page slots (slot = page * P +
+    offset, -1 skips): 64 e2m1 data bytes and 4 e8m0 scale bytes per token,
+    OCP MX conversion. Writes the cache views in place."""
+    dev = _same_device(k, slot_mapping, k_data, k_scale)
+    if k.dtype != torch.bfloat16 or k.dim() != 2 or k.shape[1] != 128 or k.stride(1) != 1:
+        raise ValueError("k must be bf16 [N, 128] with contiguous head_dim")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 vector")
+    if slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping needs one entry per key row")
+    kc = _kcache(k_data, k_scale)
+    with torch.cuda.device(dev):
+        _check(lib().mxs_write_pages(k.data_ptr(), k.stride(0), k.shape[0], slot_mapping.data_ptr(), ctypes.byref(kc),
+                                     _stream(dev, stream)))

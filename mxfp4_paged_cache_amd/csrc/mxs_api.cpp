@@ -102,6 +102,51 @@ extern "C" {
 
 const char* mxs_last_error(void) { return g_error.c_str(); }
 
+int mxs_write_pages(const void* k, int64_t k_row_stride, int64_t num_tokens, const int64_t* slot_mapping,
+                    const mxs_kcache* c, void* stream) {
+  if (!c) return fail(MXS_EINVAL, "cache descriptor must not be NULL");
+  if (num_tokens < 0) return fail(MXS_EINVAL, "num_tokens must be >= 0");
+  if (c->page_size != 64 && c->page_size != 128)
+    return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", c->page_size);
+  if (num_tokens == 0) return MXS_OK;
+  if (!k || !slot_mapping) return fail(MXS_EINVAL, "keys and slot_mapping must not be NULL");
+  if (!aligned(k, 16) || k_row_stride < 128 || k_row_stride % 8)
+    return fail(MXS_ELAYOUT, "key rows must be 16-byte aligned with a row stride >= 128 elements");
+  if (!aligned(slot_mapping, 8)) return fail(MXS_ELAYOUT, "slot_mapping must be 8-byte aligned");
+  if (!c->data || !c->scale) return fail(MXS_EINVAL, "cache data and scale pointers must not be NULL");
+  const int P = c->page_size;
+  if (!aligned(c->data, 16) || !aligned(c->scale, 4)) return fail(MXS_ELAYOUT, "cache views misaligned");
+  if (c->data_page_stride < (int64_t)P * 64 || c->data_page_stride % 16 || c->scale_page_stride < (int64_t)P * 4 ||
+      c->scale_page_stride % 4)
+    return fail(MXS_ELAYOUT, "cache page strides too small or misaligned");
+  if (c->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
+  int64_t tmp;
+  if (!mul_add(c->num_pages, c->data_page_stride, 0, &tmp) || !mul_add(c->num_pages, c->scale_page_stride, 0, &tmp) ||
+      !mul_add(num_tokens, k_row_stride, 0, &tmp))
+    return fail(MXS_ELAYOUT, "span overflows 64 bits");
+  int dev;
+  DeviceInfo info;
+  int rc = current_device(&dev, &info);
+  if (rc != MXS_OK) return rc;
+  mxs::WArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.k = static_cast<const uint16_t*>(k);
+  a.k_row_stride = k_row_stride;
+  a.slots = slot_mapping;
+  a.n = num_tokens;
+  a.kd = static_cast<uint8_t*>(const_cast<void*>(c->data));
+  a.kd_page_stride = c->data_page_stride;
+  a.ks = static_cast<uint8_t*>(const_cast<void*>(c->scale));
+  a.ks_page_stride = c->scale_page_stride;
+  a.num_pages = c->num_pages;
+  a.P = P;
+  const int64_t waves = ceil_div(ceil_div(num_tokens, 4), 4);   // 4 steps of 4 tokens per wave
+  const int64_t grid = std::min<int64_t>(ceil_div(waves, mxs::kWaves), (int64_t)info.cus * 16);
+  if (mxs::launch_write(grid, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(MXS_EDEVICE, "launching the writer failed: %s", hipGetErrorString(hipGetLastError()));
+  return MXS_OK;
+}
+
 int mxs_select_pages(int32_t mode, const mxs_batch* bt, int32_t num_heads, int32_t page_size,
                      const float* block_scores, int64_t bs_row_stride, int64_t bs_head_stride, int32_t k,
                      int32_t* pages, int64_t pages_row_stride, int64_t pages_head_stride, void* stream) {

@@ -87,8 +87,23 @@ struct SArgs {
 };
 constexpr int kSelectMaxPages = 64 * 64;   // scores per (row, head) the selection kernel holds (64 per lane)
 
+// Arguments of the writer kernel (mxs_write.hip).
+struct WArgs {
+  const uint16_t* k;        // bf16 keys [n, 128]
+  int64_t k_row_stride;     // elements
+  const int64_t* slots;     // [n]: page * P + offset, or -1
+  int64_t n;
+  uint8_t* kd;
+  int64_t kd_page_stride;   // bytes
+  uint8_t* ks;
+  int64_t ks_page_stride;   // bytes
+  int64_t num_pages;
+  int32_t P;
+};
+
 // Launchers. Return the HIP status of the launch.
 hipError_t launch_select(int per, int64_t grid, const SArgs& a, hipStream_t stream);
+hipError_t launch_write(int64_t grid, const WArgs& a, hipStream_t stream);
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream);

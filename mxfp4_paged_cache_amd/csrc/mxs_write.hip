@@ -1,0 +1,93 @@
+// MXFP4 index-K writer (gfx950): bf16 keys [N, 128] quantized into their
+// page slots (ATOM #2770, "Summary" and the write-path commit: the index key
+// is quantized straight into its pool page slot; the conversion rule is not
+// on the pages, this library follows the OCP Microscaling v1.0 conversion for
+// FP4 E2M1 elements with an E8M0 scale per 32 elements):
+//   e = floor(log2(amax)) - 2 per 32-element block, stored as byte e + 127
+//   clipped to [1, 254]; each element is the e2m1 value nearest to x / 2^e,
+//   ties to the even code, saturated at 6, sign kept.
+#include "mxs_device.h"
+
+namespace mxs {
+namespace {
+using namespace dev;
+
+// e2m1 magnitude code of a >= 0 (the scaled element): one step per midpoint
+// of the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6; at a midpoint the step is taken
+// only toward an even code, which makes ties go to the even code; past 5 the
+// code stays 7 (6.0), which saturates.
+__device__ __forceinline__ uint32_t e2m1_magnitude(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+}
+
+// Four tokens per step: lanes 16 s .. 16 s + 15 hold token 4 j + s, lane l
+// of a token holds elements 8 l .. 8 l + 7 (one 16-byte load, one 4-byte
+// store), and the 4 lanes 4 b .. 4 b + 3 one 32-element block (the block
+// maximum takes two lane exchanges). A wave takes kWriteSteps steps at once,
+// all loads first, so that enough bytes are in flight to cover the latency.
+constexpr int kWriteSteps = 4;
+
+__global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4, l = lane & 15;
+  const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  const int64_t quads = (a.n + 3) / 4;
+  for (int64_t w = w0; w * kWriteSteps < quads; w += nw) {
+    int64_t slot[kWriteSteps], page[kWriteSteps];
+    bool ok[kWriteSteps];
+    uint4 raw[kWriteSteps];
+#pragma unroll
+    for (int u = 0; u < kWriteSteps; ++u) {
+      const int64_t t = 4 * (w * kWriteSteps + u) + sub;
+      const bool tok = t < a.n;
+      slot[u] = tok ? a.slots[t] : -1;
+      page[u] = slot[u] >= 0 ? slot[u] / a.P : -1;
+      ok[u] = tok && slot[u] >= 0 && page[u] < a.num_pages;   // slots outside the pool are skipped
+      // 8 bf16 elements (16 bytes); a skipped token reads row 0, which exists
+      raw[u] = *reinterpret_cast<const uint4*>(a.k + (ok[u] ? t : 0) * a.k_row_stride + 8 * l);
+    }
+#pragma unroll
+    for (int u = 0; u < kWriteSteps; ++u) {
+      const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w4[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      int ex = 0;
+      (void)frexpf(amax, &ex);                                   // amax = m 2^ex, m in [0.5, 1)
+      const int byte = amax > 0.0f ? min(254, max(1, ex - 1 - 2 + 127)) : 1;
+      const int e = byte - 127;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = ldexpf(x[i], -e);                        // exact: a power-of-two scaling
+        const uint32_t code = e2m1_magnitude(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+        packed |= code << (4 * i);
+      }
+      if (ok[u]) {
+        const int64_t off = slot[u] - page[u] * a.P;
+        *reinterpret_cast<uint32_t*>(a.kd + page[u] * a.kd_page_stride + off * 64 + 4 * l) = packed;
+        if ((l & 3) == 0) a.ks[page[u] * a.ks_page_stride + off * 4 + (l >> 2)] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write(int64_t grid, const WArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<WArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&k_write), dim3((uint32_t)grid), dim3(kThreads), args, 0,
+                         stream);
+}
+
+}  // namespace mxs

@@ -56,6 +56,7 @@ class Workload:
     max_seq_len: Optional[int] = None
     tables: int = 1                 # disjoint block tables (benchmark rotation)
     select_k: int = 0               # > 0: the workload is top-k page selection over this prefill's block scores
+    write_tokens: int = 0           # > 0: the workload is writing this many bf16 keys into page slots
     note: str = ""
 
     @property
@@ -244,6 +245,12 @@ def select_after_prefill_long() -> Workload:
     return wl
 
 
+def write_1m_tokens() -> Workload:
+    """Writing 1,048,576 bf16 keys (8192 whole 128-token pages in random page order) into a 300k-page pool."""
+    return Workload("write_1m_tokens_p128", "prefill", H=1, page_size=128, q_lens=[1], prefix_lens=[0],
+                    seq_lens=[1], pool_pages=300_000, write_tokens=1 << 20)
+
+
 CONFIGS = {
     1: prefill_small,
     2: decode_b64_128k,
@@ -251,4 +258,5 @@ CONFIGS = {
     4: prefill_chunk,
     5: logits_shared_pool,
     6: select_after_prefill_long,
+    7: write_1m_tokens,
 }

@@ -217,6 +217,21 @@ def test_select_pages_rejections_before_device_work(L):
     assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4, rs=64 * 4097, hs=4097) == mx.MXS_EUNSUPPORTED
 
 
+def test_write_pages_rejections_before_device_work(L):
+    q, k, b, bs, lg = valid_args()
+    w = lambda kp, rs, n, slots, kc: L.mxs_write_pages(kp, rs, n, slots, ctypes.byref(kc) if kc else None, None)
+    assert w(FAKE, 128, 4, FAKE + 0x1000, None) == mx.MXS_EINVAL
+    assert w(FAKE, 128, -1, FAKE + 0x1000, k) == mx.MXS_EINVAL
+    assert w(FAKE, 128, 0, None, k) == mx.MXS_OK                          # nothing to write
+    assert w(None, 128, 4, FAKE + 0x1000, k) == mx.MXS_EINVAL
+    assert w(FAKE + 8, 128, 4, FAKE + 0x1000, k) == mx.MXS_ELAYOUT          # misaligned key rows
+    assert w(FAKE, 100, 4, FAKE + 0x1000, k) == mx.MXS_ELAYOUT              # row stride < 128
+    assert w(FAKE, 128, 4, FAKE + 0x1004, k) == mx.MXS_ELAYOUT              # misaligned slot_mapping
+    bad = mx.KCache.from_buffer_copy(bytes(k))
+    bad.data_page_stride = 100
+    assert w(FAKE, 128, 4, FAKE + 0x1000, bad) == mx.MXS_ELAYOUT
+
+
 def test_python_layer_rejects_cpu_tensors():
     import torch
     q = torch.zeros((1, 1, 128), dtype=torch.bfloat16)
