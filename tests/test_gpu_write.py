@@ -35,6 +35,9 @@ def make_keys(rng, n):
         blk[0] = np.float32(6.0 * 2.0 ** e)                     # amax in [4, 8) * 2^e keeps the scale at e
         x[t, 64:96] = blk
     bits = (x.view(np.uint32) >> 16).astype(np.uint16)          # exact bf16 patterns (truncation)
+    # subnormal bf16 blocks (magnitudes 2^-133 .. 2^-127): the scale clips to 2^-126
+    for t in range(3, n, 50):
+        bits[t, 96:128] = rng.integers(1, 0x80, 32).astype(np.uint16) | (rng.integers(0, 2, 32) << 15).astype(np.uint16)
     return bits
 
 
