@@ -70,12 +70,17 @@ def kernel_name(wl) -> str:
     return "k_logits" if (wl.mode == "logits" or wl.want_logits) else "k_prefill"
 
 
-def kernel_source_hash() -> str:
-    """Hash of everything the kernels are compiled from (device sources, the
-    headers they include, the build flags); host-only code is left out."""
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of everything one kernel is compiled and launched from: its own
+    device source, the shared headers, the planner that sets its launch shape
+    and the build flags (a change to another kernel leaves it as it was)."""
     pkg = os.path.join(ROOT, "mxfp4_paged_cache_amd")
-    files = (sorted(glob.glob(os.path.join(pkg, "csrc", "*.hip")) + glob.glob(os.path.join(pkg, "csrc", "*.h"))) +
-             [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "mxscore.h")])
+    own = os.path.join(pkg, "csrc", "mxs_" + kernel[len("k_"):] + ".hip")
+    if not os.path.exists(own):
+        raise RuntimeError(f"no device source for kernel {kernel}")
+    files = ([own] + sorted(glob.glob(os.path.join(pkg, "csrc", "*.h"))) +
+             [os.path.join(pkg, "csrc", "mxs_api.cpp"), os.path.join(pkg, "build.py"),
+              os.path.join(ROOT, "include", "mxscore.h")])
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -163,7 +168,7 @@ def main():
         from mxfp4_paged_cache_amd import workloads as W
         wl = W.CONFIGS[args.config]()
         rec = pmc_summary(args.pmc_summary).get(kernel_name(wl), {})
-        rec = {"workload": wl.name, "kernel": kernel_name(wl), "source_hash": kernel_source_hash(),
+        rec = {"workload": wl.name, "kernel": kernel_name(wl), "source_hash": kernel_source_hash(kernel_name(wl)),
                "copy_probe_bytes": COPY_PROBE_BYTES, **rec}
         if "read" in rec and "write" in rec:
             rec["bytes_per_launch"] = rec["read"]["bytes"] + rec["write"]["bytes"]
@@ -298,7 +303,7 @@ def main():
         with open(tpath) as f:
             tr = json.load(f)
         # counters taken on other kernel code no longer describe this kernel
-        if tr.get("workload") == wl.name and tr.get("source_hash") == kernel_source_hash():
+        if tr.get("workload") == wl.name and tr.get("source_hash") == kernel_source_hash(kernel_name(wl)):
             traffic = tr.get("bytes_per_launch")
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
