@@ -33,6 +33,8 @@ _SRC = os.path.join(_HERE, "mxs_oracle.c")
 
 MXO_Q_BF16 = 1
 MXO_Q_E4M3 = 2
+MXO_K_MXFP4 = 0
+MXO_K_E4M3 = 1
 MXO_MODE_PREFILL = 0
 MXO_MODE_DECODE = 1
 
@@ -73,6 +75,7 @@ class _Args(ctypes.Structure):
         ("rows", ctypes.c_void_p),
         ("num_rows", ctypes.c_int),
         ("num_threads", ctypes.c_int),
+        ("k_dtype", ctypes.c_int),
     ]
 
 
@@ -94,6 +97,9 @@ def lib():
         L.mxo_bf16_to_e4m3.argtypes = [ctypes.c_int]
         L.mxo_round_scaled_sum.restype = ctypes.c_float
         L.mxo_round_scaled_sum.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), ctypes.c_float]
+        L.mxo_round_scaled_terms.restype = ctypes.c_float
+        L.mxo_round_scaled_terms.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_float]
         L.mxo_score.restype = ctypes.c_int
         L.mxo_score.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.mxo_total_rows.restype = ctypes.c_int
@@ -126,6 +132,13 @@ def bf16_to_e4m3_table() -> np.ndarray:
     return np.array([L.mxo_bf16_to_e4m3(b) for b in range(65536)], dtype=np.uint8)
 
 
+def round_scaled_terms(S, ex, frac_bits: int, sm_scale: float) -> float:
+    n = len(S)
+    Sa = (ctypes.c_double * n)(*[float(x) for x in S])
+    ea = (ctypes.c_int * n)(*[int(x) for x in ex])
+    return lib().mxo_round_scaled_terms(Sa, ea, n, frac_bits, ctypes.c_float(sm_scale))
+
+
 def round_scaled_sum(S, s, sm_scale: float) -> float:
     Sa = (ctypes.c_double * 4)(*[float(x) for x in S])
     sa = (ctypes.c_int * 4)(*[int(x) for x in s])
@@ -146,19 +159,23 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data
 
 
-def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale: np.ndarray,
+def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale: Optional[np.ndarray],
           page_size: int, block_table: np.ndarray, seq_lens: np.ndarray, max_seq_len: int,
           sm_scale: float, cu_seqlens_q: Optional[np.ndarray] = None,
           prefix_lens: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
           want_logits: bool = True, want_blocks: bool = True, want_mags: bool = False,
           data_page_stride: Optional[int] = None, scale_page_stride: Optional[int] = None,
-          num_pages: Optional[int] = None, num_threads: int = 0) -> Result:
+          num_pages: Optional[int] = None, num_threads: int = 0, k_dtype: str = "mxfp4") -> Result:
     """Run the C oracle on host arrays.
 
     ``q``: uint16 bf16 bits or uint8 e4m3 bytes, shape [rows, H, 128] with any
     element strides; ``k_data``/``k_scale``: uint8 arrays whose first axis is the
     page (page strides taken from the arrays unless given, in bytes).
+    ``k_dtype``: "mxfp4" (e2m1 data [pages, P, 64] + e8m0 scales [pages, P, 4])
+    or "e4m3" (data [pages, P, 128] of e4m3 bytes, unit scale; k_scale None).
     """
+    if k_dtype not in ("mxfp4", "e4m3"):
+        raise ValueError(k_dtype)
     q = np.asarray(q)
     if q_dtype == "bf16":
         assert q.dtype == np.uint16
@@ -182,8 +199,10 @@ def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale
     a.num_heads = H
     a.k_data = k_data.ctypes.data
     a.data_page_stride = data_page_stride if data_page_stride is not None else k_data.strides[0]
-    a.k_scale = k_scale.ctypes.data
-    a.scale_page_stride = scale_page_stride if scale_page_stride is not None else k_scale.strides[0]
+    a.k_dtype = MXO_K_E4M3 if k_dtype == "e4m3" else MXO_K_MXFP4
+    if k_dtype == "mxfp4":
+        a.k_scale = k_scale.ctypes.data
+        a.scale_page_stride = scale_page_stride if scale_page_stride is not None else k_scale.strides[0]
     a.page_size = page_size
     a.num_pages = num_pages if num_pages is not None else k_data.shape[0]
     a.block_table = bt.ctypes.data

@@ -123,13 +123,20 @@ def token_k(data_page: bytes, scale_page: bytes, slot: int) -> List[Optional[Fra
     return out
 
 
+def token_k_e4m3(data_page: bytes, slot: int) -> List[Optional[Fraction]]:
+    """fp8 index cache: 128 e4m3 bytes per token, unit scale."""
+    return [e4m3(data_page[slot * 128 + e]) for e in range(128)]
+
+
 def score(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size: int,
           block_table, seq_lens, max_seq_len: int, sm_scale: float, cu_seqlens_q=None,
-          prefix_lens=None):
+          prefix_lens=None, k_dtype: str = "mxfp4"):
     """Brute force over every (row, head, token).
 
     ``q_rows[r][h]`` is a list of 128 ints (bf16 bits or e4m3 bytes);
-    ``pages_data[p]``/``pages_scale[p]`` are bytes objects of P*64 / P*4 bytes.
+    ``pages_data[p]``/``pages_scale[p]`` are bytes objects of P*64 / P*4 bytes
+    (k_dtype "mxfp4"), or ``pages_data[p]`` holds P*128 e4m3 bytes and
+    ``pages_scale`` is unused (k_dtype "e4m3").
     Returns (logits[r][h][t], blocks[r][h][j]) as nested lists of Python floats
     holding fp32 values.
     """
@@ -152,7 +159,10 @@ def score(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size
         qh = [decode_q(q_rows[r][h], q_dtype) for h in range(H)]
         for t in range(limit):
             page = block_table[b][t // page_size]
-            kv = token_k(pages_data[page], pages_scale[page], t % page_size)
+            if k_dtype == "e4m3":
+                kv = token_k_e4m3(pages_data[page], t % page_size)
+            else:
+                kv = token_k(pages_data[page], pages_scale[page], t % page_size)
             for h in range(H):
                 if any(v is None for v in kv) or any(v is None for v in qh[h]):
                     val = float("nan")

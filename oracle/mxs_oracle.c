@@ -23,6 +23,11 @@
  * 2^-10 below 2^12, so each 32-element block sum S_k is exact in double. The
  * four block sums are then scaled by their e8m0 factors and by sm_scale and
  * summed in a 384-bit integer, and the total is rounded once to fp32.
+ *
+ * The fp8 index cache that the MXFP4 one replaces (aiter #7061, "Summary"
+ * and "Kernels": 128 B of e4m3 per token against 68 B, 16 KB per 128-token
+ * page) is read as K(p, j, e) = e4m3(byte e of token j), unit scale; the
+ * same query, mask, logit and block rules apply.
  */
 #include "mxs_oracle.h"
 
@@ -134,32 +139,41 @@ static uint64_t big_bits(const big384* a, int lo, int n) {   /* n <= 32 */
   return r;
 }
 
-float mxo_round_scaled_sum(const double S[4], const int s[4], float sm_scale) {
+float mxo_round_scaled_terms(const double* S, const int* ex, int n, int frac_bits, float sm_scale) {
   big384 acc;
   int k, sm_exp, base = 0, have = 0, h = -1, lsb, neg, i;
-  int64_t n[4], sm_int;
+  int64_t sm_int;
   double frac;
   memset(&acc, 0, sizeof acc);
-  for (k = 0; k < 4; ++k) {
-    double t = S[k] * 1024.0;
-    if (s[k] == 255 || isnan(S[k])) return NAN;
-    n[k] = (int64_t)t;
-    if ((double)n[k] != t) abort();   /* block sums are multiples of 2^-10 */
+  if (n < 0 || n > 8) return NAN;
+  for (k = 0; k < n; ++k) {
+    double t = ldexp(S[k], frac_bits);
+    if (isnan(S[k]) || !(fabs(t) < ldexp(1.0, 62)) || t != nearbyint(t)) return NAN;
   }
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return NAN;
   frac = frexp((double)sm_scale, &sm_exp);     /* sm_scale = frac * 2^sm_exp */
   sm_int = (int64_t)ldexp(frac, 24);           /* 24-bit integer significand */
   sm_exp -= 24;
-  /* term k = n[k] * sm_int * 2^(s[k] - 127 - 10 + sm_exp) */
-  for (k = 0; k < 4; ++k) {
-    int e = s[k] - 137 + sm_exp;
-    if (n[k] == 0) continue;
+  /* term k = N_k * sm_int * 2^(ex[k] - frac_bits + sm_exp), N_k = S[k] * 2^frac_bits */
+  for (k = 0; k < n; ++k) {
+    int e = ex[k] - frac_bits + sm_exp;
+    if (S[k] == 0.0) continue;
     if (!have || e < base) base = e;
     have = 1;
   }
   if (!have) return 0.0f;
-  for (k = 0; k < 4; ++k)
-    if (n[k] != 0) big_add_shifted(&acc, n[k] * sm_int, s[k] - 137 + sm_exp - base);
+  for (k = 0; k < n; ++k) {
+    int64_t N, hi, lo, sg;
+    int sh;
+    if (S[k] == 0.0) continue;
+    N = (int64_t)ldexp(S[k], frac_bits);
+    sg = N < 0 ? -1 : 1;
+    hi = (sg * N) >> 31;                       /* |N| = hi * 2^31 + lo, both below 2^31 */
+    lo = (sg * N) & 0x7FFFFFFF;
+    sh = ex[k] - frac_bits + sm_exp - base;
+    if (hi) big_add_shifted(&acc, sg * hi * sm_int, sh + 31);
+    if (lo) big_add_shifted(&acc, sg * lo * sm_int, sh);
+  }
   neg = (int)(acc.w[5] >> 63);
   if (neg) {   /* magnitude */
     uint64_t carry = 1;
@@ -192,6 +206,16 @@ float mxo_round_scaled_sum(const double S[4], const int s[4], float sm_scale) {
   }
 }
 
+float mxo_round_scaled_sum(const double S[4], const int s[4], float sm_scale) {
+  int ex[4], k;
+  for (k = 0; k < 4; ++k) {
+    if (s[k] == 255 || isnan(S[k])) return NAN;
+    if (ldexp(S[k], 10) != nearbyint(ldexp(S[k], 10))) abort();   /* block sums are multiples of 2^-10 */
+    ex[k] = s[k] - 127;
+  }
+  return mxo_round_scaled_terms(S, ex, 4, 10, sm_scale);
+}
+
 /* ------------------------------------------------------------ scoring */
 
 int mxo_total_rows(const mxo_args* a) {
@@ -221,7 +245,9 @@ static double q_hat(const mxo_args* a, int64_t row, int h, int e) {
 int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
   int T, R, H, P, NB, W, err = 0;
   int64_t ri;
-  if (!a || !a->q || !a->k_data || !a->k_scale || !a->block_table || !a->seq_lens) return -1;
+  if (!a || !a->q || !a->k_data || !a->block_table || !a->seq_lens) return -1;
+  if (a->k_dtype != MXO_K_MXFP4 && a->k_dtype != MXO_K_E4M3) return -1;
+  if (a->k_dtype == MXO_K_MXFP4 && !a->k_scale) return -1;
   if (a->mode == MXO_MODE_PREFILL && (!a->cu_seqlens_q || !a->prefix_lens)) return -1;
   if (a->q_dtype != MXO_Q_BF16 && a->q_dtype != MXO_Q_E4M3) return -1;
   if (a->num_heads <= 0 || a->page_size <= 0 || a->batch < 0 || a->max_seq_len < 0) return -1;
@@ -274,6 +300,35 @@ int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
       if (j >= a->bt_width) { err = -2; break; }
       page = a->block_table[(int64_t)b * a->bt_row_stride + j];
       if (page < 0 || page >= a->num_pages) { err = -2; break; }
+      if (a->k_dtype == MXO_K_E4M3) {
+        /* fp8 cache: 128 e4m3 bytes per token, unit scale. Products of two
+           e4m3 values are multiples of 2^-18 below 2^18, so every block sum
+           is exact in double; the four sums go to the exact rounding with
+           exponent 0. */
+        dp = a->k_data + page * a->data_page_stride + (int64_t)slot * 128;
+        for (h = 0; h < H; ++h) {
+          double S[4], mag = 0.0;
+          int ex[4] = {0, 0, 0, 0};
+          float logit;
+          for (k = 0; k < 4; ++k) {
+            double sum = 0.0;
+            for (e = 32 * k; e < 32 * k + 32; ++e) {
+              double p = qv[h * 128 + e] * mxo_e4m3_value(dp[e]);
+              sum += p;
+              mag += fabs(p);
+            }
+            S[k] = sum;
+          }
+          logit = mxo_round_scaled_terms(S, ex, 4, 18, a->sm_scale);
+          if (logits) logits[((int64_t)ri * H + h) * W + t] = logit;
+          if (mags) mags[((int64_t)ri * H + h) * W + t] = mag;
+          if (blocks) {
+            float* bp = &blocks[((int64_t)ri * H + h) * NB + j];
+            if (logit > *bp) *bp = logit;
+          }
+        }
+        continue;
+      }
       dp = a->k_data + page * a->data_page_stride + (int64_t)slot * 64;
       sp = a->k_scale + page * a->scale_page_stride + (int64_t)slot * 4;
       for (e = 0; e < 128; ++e) {

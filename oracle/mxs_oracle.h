@@ -12,6 +12,9 @@
  *   - Page of P tokens: data view [page][token][64 B], scale view
  *     [page][token][4 B], each with its own byte page stride (aiter #7061,
  *     "Format"; aiter #5518, "Summary").
+ *   - fp8 index cache (the format the MXFP4 one replaces; aiter #7061,
+ *     "Summary": 128 B per token): data view [page][token][128 B] of e4m3
+ *     values, unit scale, no scale view.
  *   - Query: bf16 rounded to e4m3 (round to nearest even, saturating at 448,
  *     unit scale), or e4m3 bytes used as stored (aiter #7061, "Kernels";
  *     ATOM #2770, the write-path commit on the unit-scale saturating e4m3 q).
@@ -31,6 +34,8 @@ extern "C" {
 
 #define MXO_Q_BF16 1
 #define MXO_Q_E4M3 2
+#define MXO_K_MXFP4 0
+#define MXO_K_E4M3 1
 #define MXO_MODE_PREFILL 0
 #define MXO_MODE_DECODE 1
 
@@ -46,14 +51,19 @@ int mxo_bf16_to_e4m3(int bf16_bits);
  * 32-element block sums of e4m3 x e2m1 products). Returns NaN for byte 255. */
 float mxo_round_scaled_sum(const double S[4], const int s[4], float sm_scale);
 
+/* RN_fp32(sm_scale * sum_k S[k] * 2^ex[k]) for n <= 8 terms, computed exactly
+ * then rounded once. Each S[k] * 2^frac_bits must be an integer below 2^62 in
+ * magnitude (NaN is returned otherwise). */
+float mxo_round_scaled_terms(const double* S, const int* ex, int n, int frac_bits, float sm_scale);
+
 typedef struct mxo_args {
   int mode;                         /* MXO_MODE_PREFILL or MXO_MODE_DECODE */
   int q_dtype;                      /* MXO_Q_BF16 (uint16 bits) or MXO_Q_E4M3 (bytes) */
   const void* q;                    /* prefill: [T, H, 128]; decode: [B, H, 128] */
   int64_t q_row_stride, q_head_stride;   /* elements */
   int num_heads;
-  const uint8_t* k_data; int64_t data_page_stride;    /* bytes */
-  const uint8_t* k_scale; int64_t scale_page_stride;  /* bytes */
+  const uint8_t* k_data; int64_t data_page_stride;    /* bytes; token stride 64 (MXFP4) or 128 (e4m3) */
+  const uint8_t* k_scale; int64_t scale_page_stride;  /* bytes; MXFP4 only (NULL for e4m3) */
   int page_size;                    /* tokens per page */
   int64_t num_pages;                /* bound check on block-table entries */
   const int32_t* block_table; int64_t bt_row_stride; int bt_width;
@@ -66,6 +76,7 @@ typedef struct mxo_args {
   const int32_t* rows;              /* optional subset of query rows (NULL = all rows) */
   int num_rows;                     /* rows in the subset (ignored when rows == NULL) */
   int num_threads;                  /* 0 = OpenMP default */
+  int k_dtype;                      /* MXO_K_MXFP4 (e2m1 + e8m0 views) or MXO_K_E4M3 (128 e4m3 bytes per token) */
 } mxo_args;
 
 /* Score the selected rows. Outputs are dense and row-major over the selected
