@@ -29,7 +29,8 @@ the roofline picks up while the kernel sources still hash the same.
 3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
 5: logits, 64-token pages in a shared pool past 4.608e9 bytes, 6: top-64 page
 selection over the block scores of config 3, 7: writing 2^20 bf16 keys into
-MXFP4 page slots).
+MXFP4 page slots; 8, 9, 10: configs 2, 3 and 7 over an fp8 (e4m3, 128 B per
+token) index cache, the format the MXFP4 one replaces).
 """
 from __future__ import annotations
 
@@ -124,19 +125,29 @@ def pmc_summary(dbs):
     return out
 
 
+def path_dtype(wl) -> str:
+    """The arithmetic type the measured path computes in."""
+    if wl.write_tokens:
+        return "bf16 -> e4m3" if wl.k_dtype == "e4m3" else "bf16 -> e2m1 + e8m0"
+    if wl.select_k:
+        return "f32"
+    return "e4m3 x e4m3 -> f32" if wl.k_dtype == "e4m3" else "e2m1 x e4m3 -> f32"
+
+
 def algorithmic_bytes(wl, inp) -> int:
     """Bytes a call must move at minimum: every live page once (data + scales),
     the query rows, the block-table entries of live pages, and every output
     element written once."""
+    token_bytes = 128 if wl.k_dtype == "e4m3" else 68     # fp8 cache: 128 e4m3 bytes; MXFP4: 64 + 4
     if wl.write_tokens:
-        # the writer reads each bf16 key (256 B) and its slot (8 B) and writes 64 + 4 B
-        return wl.write_tokens * (256 + 8 + 68)
+        # the writer reads each bf16 key (256 B) and its slot (8 B) and writes one cache token
+        return wl.write_tokens * (256 + 8 + token_bytes)
     if wl.select_k:
         # the selection reads every block score and writes k page ids per (row, head)
         return wl.T * wl.H * (wl.NB + wl.select_k) * 4 + (wl.B * 3 + 1) * 4
     P = wl.page_size
     pages = sum((min(s, wl.window) + P - 1) // P for s in wl.seq_lens)
-    kbytes = pages * P * 68
+    kbytes = pages * P * token_bytes
     qbytes = wl.T * wl.H * 128 * (2 if wl.q_dtype == "bf16" else 1)
     table = pages * 4
     out = 0
@@ -208,7 +219,8 @@ def main():
 
     bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if wl.want_blocks else None
     lg = torch.empty((T, H, Wd), dtype=torch.float32, device=dev) if wl.want_logits else None
-    plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks)
+    plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks,
+                        k_dtype=wl.k_dtype)
     log(f"plan: {plan.as_dict()}")
 
     sel = None
@@ -334,10 +346,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 x e4m3 -> f32",
+        "dtype": path_dtype(wl),
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "query_rows": T, "heads": H, "head_dim": 128,
-                   "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype,
+                   "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype, "cache": wl.k_dtype,
                    "e8m0_range": [wl.scale_lo, wl.scale_hi], "outputs": ("block_scores" if wl.want_blocks else "") +
                    ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables),
                    **({"select_k": wl.select_k} if wl.select_k else {}),
@@ -365,10 +377,15 @@ def cpu_baseline_write(wl, wk, wslots, sample_tokens: int):
     n = sample_tokens or 8192
     bits = wk[:n].view(torch.int16).cpu().numpy().view(np.uint16)
     P = wl.page_size
-    kd = np.zeros((n // P + 1, P, 64), np.uint8)
-    ks = np.zeros((n // P + 1, P, 4), np.uint8)
-    t0 = time.perf_counter()
-    writer.write_pages(bits, np.arange(n), kd, ks, P)
+    if wl.k_dtype == "e4m3":
+        kd = np.zeros((n // P + 1, P, 128), np.uint8)
+        t0 = time.perf_counter()
+        writer.write_pages_e4m3(bits, np.arange(n), kd, P)
+    else:
+        kd = np.zeros((n // P + 1, P, 64), np.uint8)
+        ks = np.zeros((n // P + 1, P, 4), np.uint8)
+        t0 = time.perf_counter()
+        writer.write_pages(bits, np.arange(n), kd, ks, P)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} of {wl.write_tokens} keys, {dt:.2f} s"}
@@ -423,7 +440,7 @@ def cpu_baseline(wl, inp, sample_rows: int):
     used = np.unique(bt[bt >= 0])
     idx = torch.as_tensor(used, dtype=torch.long, device=inp.k_data.device)
     kd = inp.k_data.index_select(0, idx).cpu().numpy()
-    ks = inp.k_scale.index_select(0, idx).cpu().numpy()
+    ks = inp.k_scale.index_select(0, idx).cpu().numpy() if inp.k_scale is not None else None
     remap = np.full(int(bt.max()) + 1, -1, np.int64)
     remap[used] = np.arange(len(used))
     bt = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
@@ -433,7 +450,7 @@ def cpu_baseline(wl, inp, sample_rows: int):
     oracle.score(mode=mode, q=q, q_dtype=wl.q_dtype, k_data=kd, k_scale=ks, page_size=wl.page_size, block_table=bt,
                  seq_lens=inp.seq_lens.cpu().numpy(), max_seq_len=wl.window, sm_scale=float(np.float32(1 / np.sqrt(128))),
                  cu_seqlens_q=cu, prefix_lens=inp.prefix_lens.cpu().numpy(), rows=rows,
-                 want_logits=wl.want_logits, want_blocks=wl.want_blocks, num_threads=threads)
+                 want_logits=wl.want_logits, want_blocks=wl.want_blocks, num_threads=threads, k_dtype=wl.k_dtype)
     dt = time.perf_counter() - t0
     return {"value": sample_triples / dt, "unit": "(row\u00d7head\u00d7token)/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {T} query rows ({sample_triples} live triples, all heads and pages of "

@@ -17,6 +17,14 @@
  * shared multi-slot pool past 4 GiB are all expressed this way; page offsets
  * are computed in 64 bits.
  *
+ * fp8 index cache (the format the MXFP4 one replaces; aiter #7061,
+ * "Summary": 128 B of e4m3 per token against 68 B, and "Kernels": a
+ * 16 KB buffer per 128-token page): k_dtype = MXS_K_E4M3 selects pages of
+ * 128 e4m3 (OCP float8_e4m3fn) bytes per token with unit scale, element e
+ * at byte e; the data view is the only view:
+ *     data  byte e of token j of page p: data  + p*data_page_stride  + j*128 + e
+ * Everything else (query, mask, scores, outputs) is the same for both.
+ *
  * Query (aiter #7061, "Kernels"; ATOM #2770, write-path commit): 128
  * elements per (row, head), bf16 rounded in-kernel to e4m3 (nearest even,
  * saturating at +-448, unit scale), or e4m3 (OCP float8_e4m3fn) used as stored.
@@ -37,6 +45,8 @@
  * group keeps about 12 bits below the group's largest product. Results equal
  * RN_fp32 of the exact dot except under cancellation, with
  * |error| <= 2^-11 * sum_e |Q_hat[e] K[e]| in the worst measured case.
+ * An fp8 cache runs the same instruction with both operands e4m3 and unit
+ * scales.
  *
  * Outputs: every element of the window is written: logits [rows, heads,
  * max_seq_len] and block scores [rows, heads, ceil(max_seq_len / P)]; live
@@ -52,7 +62,8 @@
  * may be captured in a HIP graph. Device-side contract (not checked):
  * cu_seqlens_q non-decreasing with cu_seqlens_q[B] == total_rows, each
  * request's q_len <= max_query_len, block-table entries of live pages in
- * [0, num_pages), e8m0 bytes of live tokens in [1, 254]. Entries past a
+ * [0, num_pages), e8m0 bytes (MXFP4) of live tokens in [1, 254], no NaN
+ * e4m3 byte (0x7F, 0xFF) in live tokens of an fp8 cache. Entries past a
  * request's live pages are never read (they may hold -1).
  *
  * Thread safety: calls may be made from several host threads; error text is
@@ -70,7 +81,7 @@ extern "C" {
 /* ---------------------------------------------------------------- status */
 #define MXS_OK 0
 #define MXS_EINVAL (-1)       /* null pointer, negative count, sm_scale not finite and > 0 */
-#define MXS_EDTYPE (-2)       /* query dtype is neither bf16 nor e4m3 (fp16 is refused) */
+#define MXS_EDTYPE (-2)       /* query dtype not bf16 / e4m3 (fp16 is refused), or unknown cache dtype */
 #define MXS_ELAYOUT (-3)      /* stride, alignment, page size or table width rule broken */
 #define MXS_EUNSUPPORTED (-4) /* current device is not gfx950, or no device */
 #define MXS_EDEVICE (-5)      /* HIP runtime error while launching */
@@ -79,20 +90,26 @@ extern "C" {
 #define MXS_Q_BF16 1
 #define MXS_Q_E4M3 2
 
+#define MXS_K_MXFP4 0         /* cache: e2m1 data + e8m0 scales (68 B per token) */
+#define MXS_K_E4M3 1          /* cache: e4m3 data, unit scale (128 B per token) */
+
 #define MXS_MODE_PREFILL 1
 #define MXS_MODE_DECODE 2
 #define MXS_MODE_LOGITS 3
 
 /* Paged MXFP4 cache views (see the layout above).
- * data: 16-byte aligned, data_page_stride a multiple of 16 and >= 64 * page_size.
- * scale: 4-byte aligned, scale_page_stride a multiple of 4 and >= 4 * page_size. */
+ * data: 16-byte aligned, data_page_stride a multiple of 16 and >= 64 * page_size
+ * (MXS_K_E4M3: >= 128 * page_size).
+ * scale: 4-byte aligned, scale_page_stride a multiple of 4 and >= 4 * page_size
+ * (MXS_K_MXFP4 only; ignored for MXS_K_E4M3 and may be NULL). */
 typedef struct mxs_kcache {
   const void* data;
   int64_t data_page_stride;    /* bytes */
   const void* scale;
   int64_t scale_page_stride;   /* bytes */
   int32_t page_size;           /* 64 or 128 */
-  int64_t num_pages;           /* pages addressable through both views, >= 1 */
+  int32_t k_dtype;             /* MXS_K_MXFP4 (0) or MXS_K_E4M3 (1) */
+  int64_t num_pages;           /* pages addressable through the view(s), >= 1 */
 } mxs_kcache;
 
 /* Query rows: element e of head h of row r at
@@ -157,14 +174,15 @@ typedef struct mxs_plan {
   int32_t head_groups;         /* decode: groups of 64 heads */
   int64_t items;               /* total work items */
   int32_t kernel;              /* internal kernel id */
-  int32_t reserved;
+  int32_t k_dtype;             /* cache dtype the plan was made for */
 } mxs_plan;
 
 /* Compute a plan. parallel_unit_num > 0 overrides the workgroup count
  * (aiter #5518: explicit parallel_unit_num remains an override); 0 = auto.
- * For MXS_MODE_DECODE, max_query_len is ignored (1). Returns MXS_OK or an
- * error code; writes *plan only on success. */
-int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+ * For MXS_MODE_DECODE, max_query_len is ignored (1). k_dtype is the cache's
+ * (MXS_K_MXFP4 or MXS_K_E4M3). Returns MXS_OK or an error code; writes *plan
+ * only on success. */
+int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
                   int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
                   int32_t parallel_unit_num, mxs_plan* plan);
 
@@ -172,7 +190,7 @@ int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_
  * device's compute-unit count and wg_per_cu the workgroups of the chosen
  * kernel resident per CU (mxs_plan_make reads both from the current device).
  * Identical arguments always give an identical plan. */
-int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
+int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
                       int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
                       int32_t parallel_unit_num, int32_t num_cus, int32_t wg_per_cu, mxs_plan* plan);
 
@@ -207,7 +225,10 @@ int mxs_score_logits(const mxs_query* q, const mxs_kcache* k, const mxs_batch* b
  * [1, 254], and each element as the e2m1 code nearest to x / 2^e (ties to the
  * even code, saturated at 6, sign kept), element 2m in the low nibble of
  * data byte m. Writes 64 data bytes and 4 scale bytes per token into the
- * cache views and nothing else. Non-finite keys are outside the contract.
+ * cache views and nothing else. For an fp8 cache (MXS_K_E4M3) each element
+ * becomes the e4m3 byte nearest to it (ties to even, saturated at +-448,
+ * unit scale: the query rounding above), 128 bytes per token in the data
+ * view. Non-finite keys are outside the contract.
  * Two tokens with the same slot race. Asynchronous on stream; num_tokens = 0
  * is a no-op. Returns MXS_OK, MXS_EINVAL, MXS_ELAYOUT, MXS_EUNSUPPORTED or
  * MXS_EDEVICE. */
@@ -240,8 +261,8 @@ int mxs_select_pages(int32_t mode, const mxs_batch* batch, int32_t num_heads, in
 
 /* Check of the device-side contract that the scoring calls cannot verify
  * without a device-to-host copy (see "Device contract" above). Synchronous:
- * copies the request metadata (and, with check_scales, the scale bytes of
- * every live token) to host memory after the work already queued on stream,
+ * copies the request metadata (and, with check_scales, the scale bytes, or
+ * for an fp8 cache the data bytes, of every live token) to host memory after the work already queued on stream,
  * and checks, for mode MXS_MODE_PREFILL / MXS_MODE_LOGITS:
  *   cu_seqlens_q[0] == 0, non-decreasing, cu_seqlens_q[batch] == total_rows,
  *   every request's q_len <= max_query_len, prefix_lens >= 0;
@@ -249,7 +270,8 @@ int mxs_select_pages(int32_t mode, const mxs_batch* batch, int32_t num_heads, in
  *   0 <= seq_lens[b] <= max_seq_len;
  *   block-table entries of live pages (pages holding a token some row of the
  *   request sees) in [0, num_pages);
- *   with check_scales != 0: e8m0 bytes of live tokens in [1, 254].
+ *   with check_scales != 0: e8m0 bytes of live tokens in [1, 254] (MXFP4),
+ *   or no NaN byte (0x7F, 0xFF) in live tokens (fp8 cache).
  * Returns MXS_OK, or MXS_EINVAL naming the first violation (mxs_last_error),
  * or MXS_EDEVICE if a copy fails. For tests and debugging: not on the hot
  * path and not capturable in a graph. Allocates host memory only. */

@@ -11,7 +11,15 @@ works"; aiter #5518, "Summary"):
 * :func:`score_prefill` -- per-page max block scores (and optionally logits)
   for request-concatenated query rows with causal + prefix masking;
 * :func:`score_decode` -- one query row per request, limit = seq_len;
-* :func:`score_logits` -- logits-first variant of prefill.
+* :func:`score_logits` -- logits-first variant of prefill;
+* :func:`select_pages` -- top-k pages per (row, head) from block scores;
+* :func:`write_pages` -- quantize bf16 keys into their page slots;
+* :func:`check_metadata` -- synchronous check of the device-side contract.
+
+The cache is an MXFP4 one (``k_data`` [pages, P, 64] e2m1 bytes and
+``k_scale`` [pages, P, 4] e8m0 bytes) or, with ``k_scale=None``, an fp8 one
+(``k_data`` [pages, P, 128] e4m3 bytes, unit scale: the format the MXFP4
+cache replaces, aiter #7061, "Summary").
 
 Rejected inputs raise ``ValueError`` before anything is launched.
 """
@@ -24,13 +32,15 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["score_prefill", "score_decode", "score_logits", "make_plan", "library_path", "lib", "MxsError"]
+__all__ = ["score_prefill", "score_decode", "score_logits", "select_pages", "write_pages", "check_metadata",
+           "make_plan", "library_path", "lib", "MxsError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxscore.so")
 
 MXS_OK, MXS_EINVAL, MXS_EDTYPE, MXS_ELAYOUT, MXS_EUNSUPPORTED, MXS_EDEVICE = 0, -1, -2, -3, -4, -5
 MXS_Q_BF16, MXS_Q_E4M3 = 1, 2
+MXS_K_MXFP4, MXS_K_E4M3 = 0, 1
 MXS_MODE_PREFILL, MXS_MODE_DECODE, MXS_MODE_LOGITS = 1, 2, 3
 
 
@@ -47,7 +57,8 @@ class Query(ctypes.Structure):
 
 class KCache(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("data_page_stride", ctypes.c_int64), ("scale", ctypes.c_void_p),
-                ("scale_page_stride", ctypes.c_int64), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+                ("scale_page_stride", ctypes.c_int64), ("page_size", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
 
 
 class Out(ctypes.Structure):
@@ -65,7 +76,7 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "q_dtype", "page_size", "num_heads", "batch", "max_query_len", "max_seq_len", "want_logits",
         "want_blocks", "grid", "block", "slots_per_item", "pages_per_item", "slot_items", "page_items",
-        "head_groups")] + [("items", ctypes.c_int64), ("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        "head_groups")] + [("items", ctypes.c_int64), ("kernel", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -89,9 +100,9 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.POINTER
         i32 = ctypes.c_int32
-        L.mxs_plan_make.argtypes = [i32] * 10 + [P(Plan)]
+        L.mxs_plan_make.argtypes = [i32] * 11 + [P(Plan)]
         L.mxs_plan_make.restype = ctypes.c_int
-        L.mxs_plan_make_for.argtypes = [i32] * 12 + [P(Plan)]
+        L.mxs_plan_make_for.argtypes = [i32] * 13 + [P(Plan)]
         L.mxs_plan_make_for.restype = ctypes.c_int
         for name in ("mxs_score_prefill", "mxs_score_decode", "mxs_score_logits"):
             f = getattr(L, name)
@@ -143,7 +154,20 @@ def _query(q: torch.Tensor) -> Query:
     return Query(q.data_ptr(), dt, q.stride(0), q.stride(1), q.shape[1])
 
 
-def _kcache(k_data: torch.Tensor, k_scale: torch.Tensor) -> KCache:
+def _kcache(k_data: torch.Tensor, k_scale: Optional[torch.Tensor]) -> KCache:
+    if k_scale is None:
+        # fp8 index cache: [pages, page_size, 128] e4m3 bytes, unit scale, no scale view
+        if k_data.dtype not in _E4M3_DTYPES:
+            raise ValueError(f"an fp8 cache view must be float8_e4m3fn or uint8, got {k_data.dtype}")
+        if k_data.dim() != 3 or k_data.shape[2] != 128:
+            raise ValueError(f"an fp8 cache view must be [pages, page_size, 128], got {tuple(k_data.shape)}")
+        if k_data.stride(2) != 1 or k_data.stride(1) != 128:
+            raise ValueError("cache token rows must be contiguous (128 B of e4m3 per token)")
+        P = k_data.shape[1]
+        if P not in (64, 128):
+            raise ValueError(f"page size must be 64 or 128, got {P}")
+        return KCache(data=k_data.data_ptr(), data_page_stride=k_data.stride(0), scale=None, scale_page_stride=0,
+                      page_size=P, k_dtype=MXS_K_E4M3, num_pages=k_data.shape[0])
     if k_data.dtype not in _DATA_DTYPES or k_scale.dtype not in _SCALE_DTYPES:
         raise ValueError(f"cache views must be uint8 (or fp4x2 / e8m0) tensors, got {k_data.dtype} / {k_scale.dtype}")
     if k_data.dim() != 3 or k_scale.dim() != 3:
@@ -157,7 +181,8 @@ def _kcache(k_data: torch.Tensor, k_scale: torch.Tensor) -> KCache:
         raise ValueError(f"data and scale views hold different page counts ({k_data.shape[0]} vs {k_scale.shape[0]})")
     if P not in (64, 128):
         raise ValueError(f"page size must be 64 or 128, got {P}")
-    return KCache(k_data.data_ptr(), k_data.stride(0), k_scale.data_ptr(), k_scale.stride(0), P, k_data.shape[0])
+    return KCache(data=k_data.data_ptr(), data_page_stride=k_data.stride(0), scale=k_scale.data_ptr(),
+                  scale_page_stride=k_scale.stride(0), page_size=P, k_dtype=MXS_K_MXFP4, num_pages=k_data.shape[0])
 
 
 def _int_vec(name: str, t: Optional[torch.Tensor], n: int) -> int:
@@ -202,12 +227,15 @@ def _stream(device, stream) -> int:
 
 
 def make_plan(mode: str, q_dtype: torch.dtype, page_size: int, num_heads: int, batch: int, max_query_len: int,
-              max_seq_len: int, want_logits: bool, want_blocks: bool = True, parallel_unit_num: int = 0) -> Plan:
-    """Launch plan for the current device (pure function of these host integers)."""
+              max_seq_len: int, want_logits: bool, want_blocks: bool = True, parallel_unit_num: int = 0,
+              k_dtype: str = "mxfp4") -> Plan:
+    """Launch plan for the current device (pure function of these host
+    integers). k_dtype: "mxfp4" (e2m1 + e8m0 views) or "e4m3" (fp8 cache)."""
     m = {"prefill": MXS_MODE_PREFILL, "decode": MXS_MODE_DECODE, "logits": MXS_MODE_LOGITS}[mode]
     dt = MXS_Q_BF16 if q_dtype == torch.bfloat16 else MXS_Q_E4M3
+    kd = {"mxfp4": MXS_K_MXFP4, "e4m3": MXS_K_E4M3}[k_dtype]
     p = Plan()
-    _check(lib().mxs_plan_make(m, dt, page_size, num_heads, batch, max_query_len, max_seq_len, int(want_logits),
+    _check(lib().mxs_plan_make(m, dt, kd, page_size, num_heads, batch, max_query_len, max_seq_len, int(want_logits),
                                int(want_blocks), parallel_unit_num, ctypes.byref(p)))
     return p
 
@@ -349,7 +377,8 @@ def select_pages(block_scores: torch.Tensor, k: int, seq_lens, max_seq_len: int,
 def write_pages(k: torch.Tensor, slot_mapping: torch.Tensor, k_data, k_scale, stream=None) -> None:
     """Quantize bf16 keys k [N, 128] into MXFP4 page slots (slot = page * P +
     offset, -1 skips): 64 e2m1 data bytes and 4 e8m0 scale bytes per token,
-    OCP MX conversion. Writes the cache views in place."""
+    OCP MX conversion; with k_scale None, into an fp8 cache (128 e4m3 bytes
+    per token, nearest even, saturating). Writes the cache views in place."""
     dev = _same_device(k, slot_mapping, k_data, k_scale)
     if k.dtype != torch.bfloat16 or k.dim() != 2 or k.shape[1] != 128 or k.stride(1) != 1:
         raise ValueError("k must be bf16 [N, 128] with contiguous head_dim")

@@ -80,21 +80,52 @@ int current_device(int* dev, DeviceInfo* info) {
   return MXS_OK;
 }
 
-int occupancy_cached(int dev, int32_t kernel, int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
+int occupancy_cached(int dev, int32_t kernel, int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs,
+                     bool want_lg) {
   const uint64_t key = ((uint64_t)(uint32_t)dev << 32) | ((uint64_t)kernel << 16) | ((uint64_t)q_dtype << 8) |
-                       (uint64_t)(page_size == 128 ? 1 : 0) | (want_bs ? 2u : 0u) | (want_lg ? 4u : 0u);
+                       (uint64_t)(page_size == 128 ? 1 : 0) | (want_bs ? 2u : 0u) | (want_lg ? 4u : 0u) |
+                       (k_dtype == MXS_K_E4M3 ? 8u : 0u);
   {
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_occupancy.find(key);
     if (it != g_occupancy.end()) return it->second;
   }
-  const int occ = mxs::occupancy(kernel, q_dtype, page_size, want_bs, want_lg);
+  const int occ = mxs::occupancy(kernel, q_dtype, k_dtype, page_size, want_bs, want_lg);
   std::lock_guard<std::mutex> lock(g_mu);
   g_occupancy[key] = occ;
   return occ;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_k_dtype(int32_t k_dtype) {
+  if (k_dtype != MXS_K_MXFP4 && k_dtype != MXS_K_E4M3)
+    return fail(MXS_EDTYPE, "cache dtype must be MXFP4 (%d) or e4m3 (%d); got %d", MXS_K_MXFP4, MXS_K_E4M3, k_dtype);
+  return MXS_OK;
+}
+
+// The cache views of either format (page size and dtype already checked):
+// MXFP4 needs both views, an fp8 cache only the data view (128 B a token).
+int check_kcache_views(const mxs_kcache* k) {
+  const int P = k->page_size;
+  const bool fp8 = k->k_dtype == MXS_K_E4M3;
+  const int64_t token_bytes = fp8 ? 128 : 64;
+  if (!k->data || (!fp8 && !k->scale)) return fail(MXS_EINVAL, "cache data and scale pointers must not be NULL");
+  if (!aligned(k->data, 16)) return fail(MXS_ELAYOUT, "cache data view must be 16-byte aligned");
+  if (!fp8 && !aligned(k->scale, 4)) return fail(MXS_ELAYOUT, "cache scale view must be 4-byte aligned");
+  if (k->data_page_stride < (int64_t)P * token_bytes || k->data_page_stride % 16)
+    return fail(MXS_ELAYOUT, "data page stride %lld must be a multiple of 16 and >= %lld (narrow data view)",
+                (long long)k->data_page_stride, (long long)(P * token_bytes));
+  if (!fp8 && (k->scale_page_stride < (int64_t)P * 4 || k->scale_page_stride % 4))
+    return fail(MXS_ELAYOUT, "scale page stride %lld must be a multiple of 4 and >= %d (narrow scale view)",
+                (long long)k->scale_page_stride, P * 4);
+  if (k->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
+  int64_t tmp;
+  if (!mul_add(k->num_pages, k->data_page_stride, 0, &tmp) ||
+      (!fp8 && !mul_add(k->num_pages, k->scale_page_stride, 0, &tmp)))
+    return fail(MXS_ELAYOUT, "cache span overflows 64 bits");
+  return MXS_OK;
+}
 
 }  // namespace
 
@@ -108,22 +139,17 @@ int mxs_write_pages(const void* k, int64_t k_row_stride, int64_t num_tokens, con
   if (num_tokens < 0) return fail(MXS_EINVAL, "num_tokens must be >= 0");
   if (c->page_size != 64 && c->page_size != 128)
     return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", c->page_size);
+  if (check_k_dtype(c->k_dtype)) return MXS_EDTYPE;
   if (num_tokens == 0) return MXS_OK;
   if (!k || !slot_mapping) return fail(MXS_EINVAL, "keys and slot_mapping must not be NULL");
   if (!aligned(k, 16) || k_row_stride < 128 || k_row_stride % 8)
     return fail(MXS_ELAYOUT, "key rows must be 16-byte aligned with a row stride >= 128 elements");
   if (!aligned(slot_mapping, 8)) return fail(MXS_ELAYOUT, "slot_mapping must be 8-byte aligned");
-  if (!c->data || !c->scale) return fail(MXS_EINVAL, "cache data and scale pointers must not be NULL");
   const int P = c->page_size;
-  if (!aligned(c->data, 16) || !aligned(c->scale, 4)) return fail(MXS_ELAYOUT, "cache views misaligned");
-  if (c->data_page_stride < (int64_t)P * 64 || c->data_page_stride % 16 || c->scale_page_stride < (int64_t)P * 4 ||
-      c->scale_page_stride % 4)
-    return fail(MXS_ELAYOUT, "cache page strides too small or misaligned");
-  if (c->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
+  int rc0 = check_kcache_views(c);
+  if (rc0 != MXS_OK) return rc0;
   int64_t tmp;
-  if (!mul_add(c->num_pages, c->data_page_stride, 0, &tmp) || !mul_add(c->num_pages, c->scale_page_stride, 0, &tmp) ||
-      !mul_add(num_tokens, k_row_stride, 0, &tmp))
-    return fail(MXS_ELAYOUT, "span overflows 64 bits");
+  if (!mul_add(num_tokens, k_row_stride, 0, &tmp)) return fail(MXS_ELAYOUT, "span overflows 64 bits");
   int dev;
   DeviceInfo info;
   int rc = current_device(&dev, &info);
@@ -136,10 +162,11 @@ int mxs_write_pages(const void* k, int64_t k_row_stride, int64_t num_tokens, con
   a.n = num_tokens;
   a.kd = static_cast<uint8_t*>(const_cast<void*>(c->data));
   a.kd_page_stride = c->data_page_stride;
-  a.ks = static_cast<uint8_t*>(const_cast<void*>(c->scale));
+  a.ks = c->k_dtype == MXS_K_E4M3 ? nullptr : static_cast<uint8_t*>(const_cast<void*>(c->scale));
   a.ks_page_stride = c->scale_page_stride;
   a.num_pages = c->num_pages;
   a.P = P;
+  a.kdt = c->k_dtype;
   const int64_t waves = ceil_div(ceil_div(num_tokens, 4), 4);   // 4 steps of 4 tokens per wave
   const int64_t grid = std::min<int64_t>(ceil_div(waves, mxs::kWaves), (int64_t)info.cus * 16);
   if (mxs::launch_write(grid, a, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -221,7 +248,9 @@ int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, i
     return fail(MXS_EINVAL, "unknown mode %d", mode);
   if (k->page_size != 64 && k->page_size != 128)
     return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", k->page_size);
+  if (check_k_dtype(k->k_dtype)) return MXS_EDTYPE;
   const bool decode = mode == MXS_MODE_DECODE;
+  const bool fp8 = k->k_dtype == MXS_K_E4M3;
   const int32_t B = bt->batch, P = k->page_size;
   if (B < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
   if (B == 0) return MXS_OK;
@@ -279,6 +308,21 @@ int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, i
         return fail(MXS_EINVAL, "block_table[%d][%lld] = %d is outside [0, num_pages = %lld) for a live page", b,
                     (long long)j, row[j], (long long)k->num_pages);
     if (!check_scales) continue;
+    if (fp8) {
+      // live tokens of an fp8 cache must hold no NaN byte
+      sc.resize((size_t)P * 128);
+      for (int64_t j = 0; j < pages; ++j) {
+        if (!copy(sc.data(), static_cast<const uint8_t*>(k->data) + (int64_t)row[j] * k->data_page_stride, sc.size()) ||
+            hipStreamSynchronize(st) != hipSuccess)
+          return fail(MXS_EDEVICE, "copying the data of page %d failed", row[j]);
+        const int64_t ntok = std::min<int64_t>(P, live[b] - j * P);
+        for (int64_t t = 0; t < ntok * 128; ++t)
+          if ((sc[t] & 0x7F) == 0x7F)
+            return fail(MXS_EINVAL, "request %d, token %lld: e4m3 byte 0x%02X is NaN", b, (long long)(j * P + t / 128),
+                        sc[t]);
+      }
+      continue;
+    }
     sc.resize((size_t)P * 4);
     for (int64_t j = 0; j < pages; ++j) {
       if (!copy(sc.data(), static_cast<const uint8_t*>(k->scale) + (int64_t)row[j] * k->scale_page_stride, sc.size()) ||
@@ -299,15 +343,17 @@ const char* mxs_version(void) { return "mxscore 0.1 (gfx950)"; }
 // Pure planner: every input is a host integer; the same inputs give the same
 // plan. num_cus and wg_per_cu describe the device (CUs and resident
 // workgroups of the chosen kernel per CU).
-int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
-                      int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
-                      int32_t parallel_unit_num, int32_t num_cus, int32_t wg_per_cu, mxs_plan* plan) {
+int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t page_size, int32_t num_heads,
+                      int32_t batch, int32_t max_query_len, int32_t max_seq_len, int32_t want_logits,
+                      int32_t want_blocks, int32_t parallel_unit_num, int32_t num_cus, int32_t wg_per_cu,
+                      mxs_plan* plan) {
   if (!plan) return fail(MXS_EINVAL, "plan pointer is NULL");
   if (mode != MXS_MODE_PREFILL && mode != MXS_MODE_DECODE && mode != MXS_MODE_LOGITS)
     return fail(MXS_EINVAL, "unknown mode %d", mode);
   if (q_dtype != MXS_Q_BF16 && q_dtype != MXS_Q_E4M3)
     return fail(MXS_EDTYPE, "query dtype must be bf16 (%d) or e4m3 (%d); got %d (fp16 is refused)", MXS_Q_BF16,
                 MXS_Q_E4M3, q_dtype);
+  if (check_k_dtype(k_dtype)) return MXS_EDTYPE;
   if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
   if (num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", num_heads);
   if (batch < 0 || max_seq_len < 0 || (mode != MXS_MODE_DECODE && max_query_len < 0))
@@ -322,6 +368,7 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
   std::memset(&p, 0, sizeof p);
   p.mode = mode;
   p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
   p.page_size = page_size;
   p.num_heads = num_heads;
   p.batch = batch;
@@ -415,22 +462,23 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t 
   return MXS_OK;
 }
 
-int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t page_size, int32_t num_heads, int32_t batch,
-                  int32_t max_query_len, int32_t max_seq_len, int32_t want_logits, int32_t want_blocks,
-                  int32_t parallel_unit_num, mxs_plan* plan) {
+int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t page_size, int32_t num_heads,
+                  int32_t batch, int32_t max_query_len, int32_t max_seq_len, int32_t want_logits,
+                  int32_t want_blocks, int32_t parallel_unit_num, mxs_plan* plan) {
   int dev;
   DeviceInfo info;
   int rc = current_device(&dev, &info);
   if (rc != MXS_OK) return rc;
   if (q_dtype != MXS_Q_BF16 && q_dtype != MXS_Q_E4M3)
     return fail(MXS_EDTYPE, "query dtype must be bf16 or e4m3; got %d", q_dtype);
+  if (check_k_dtype(k_dtype)) return MXS_EDTYPE;
   if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
   const int32_t kid = mode == MXS_MODE_DECODE                    ? mxs::KID_DECODE
                       : (mode == MXS_MODE_LOGITS || want_logits) ? mxs::KID_LOGITS
                                                                  : mxs::KID_PREFILL;
-  const int occ = occupancy_cached(dev, kid, q_dtype, page_size, want_blocks != 0, want_logits != 0);
-  return mxs_plan_make_for(mode, q_dtype, page_size, num_heads, batch, max_query_len, max_seq_len, want_logits,
-                           want_blocks, parallel_unit_num, info.cus, occ, plan);
+  const int occ = occupancy_cached(dev, kid, q_dtype, k_dtype, page_size, want_blocks != 0, want_logits != 0);
+  return mxs_plan_make_for(mode, q_dtype, k_dtype, page_size, num_heads, batch, max_query_len, max_seq_len,
+                           want_logits, want_blocks, parallel_unit_num, info.cus, occ, plan);
 }
 
 }  // extern "C"
@@ -482,6 +530,7 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   if (q->num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", q->num_heads);
   if (k->page_size != 64 && k->page_size != 128)
     return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", k->page_size);
+  if (check_k_dtype(k->k_dtype)) return MXS_EDTYPE;
   if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return fail(MXS_EINVAL, "sm_scale must be finite and > 0");
   if (bt->batch < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
   const bool decode = mode == MXS_MODE_DECODE;
@@ -507,19 +556,10 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   if ((q->row_stride * es) % 16 || (q->head_stride * es) % 16)
     return fail(MXS_ELAYOUT, "query row and head strides must be multiples of 16 bytes (misaligned query rows)");
   // cache
-  if (!k->data || !k->scale) return fail(MXS_EINVAL, "cache data and scale pointers must not be NULL");
-  if (!aligned(k->data, 16)) return fail(MXS_ELAYOUT, "cache data view must be 16-byte aligned");
-  if (!aligned(k->scale, 4)) return fail(MXS_ELAYOUT, "cache scale view must be 4-byte aligned");
-  if (k->data_page_stride < (int64_t)P * 64 || k->data_page_stride % 16)
-    return fail(MXS_ELAYOUT, "data page stride %lld must be a multiple of 16 and >= %d (narrow data view)",
-                (long long)k->data_page_stride, P * 64);
-  if (k->scale_page_stride < (int64_t)P * 4 || k->scale_page_stride % 4)
-    return fail(MXS_ELAYOUT, "scale page stride %lld must be a multiple of 4 and >= %d (narrow scale view)",
-                (long long)k->scale_page_stride, P * 4);
-  if (k->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
-  int64_t tmp;
-  if (!mul_add(k->num_pages, k->data_page_stride, 0, &tmp) || !mul_add(k->num_pages, k->scale_page_stride, 0, &tmp))
-    return fail(MXS_ELAYOUT, "cache span overflows 64 bits");
+  {
+    const int rck = check_kcache_views(k);
+    if (rck != MXS_OK) return rck;
+  }
   // batch metadata
   if (!bt->block_table || !bt->seq_lens) return fail(MXS_EINVAL, "block_table and seq_lens must not be NULL");
   if (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens))
@@ -549,15 +589,16 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   if (rc != MXS_OK) return rc;
   mxs_plan plan;
   if (plan_in) {
-    if (plan_in->mode != mode || plan_in->q_dtype != q->dtype || plan_in->page_size != P || plan_in->num_heads != H ||
+    if (plan_in->mode != mode || plan_in->q_dtype != q->dtype || plan_in->k_dtype != k->k_dtype ||
+        plan_in->page_size != P || plan_in->num_heads != H ||
         plan_in->batch != bt->batch || plan_in->max_seq_len != bt->max_seq_len ||
         (!decode && plan_in->max_query_len != bt->max_query_len) || plan_in->want_logits != (want_lg ? 1 : 0) ||
         plan_in->want_blocks != (want_bs ? 1 : 0))
       return fail(MXS_EINVAL, "the plan was made for different shapes or outputs");
     plan = *plan_in;
   } else {
-    rc = mxs_plan_make(mode, q->dtype, P, H, bt->batch, decode ? 1 : bt->max_query_len, bt->max_seq_len, want_lg,
-                       want_bs, 0, &plan);
+    rc = mxs_plan_make(mode, q->dtype, k->k_dtype, P, H, bt->batch, decode ? 1 : bt->max_query_len, bt->max_seq_len,
+                       want_lg, want_bs, 0, &plan);
     if (rc != MXS_OK) return rc;
   }
   if (!plan_consistent(plan, mode, H, bt->batch, decode ? 1 : bt->max_query_len, NB))
@@ -572,7 +613,7 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   a.H = H;
   a.kd = static_cast<const uint8_t*>(k->data);
   a.kd_page_stride = k->data_page_stride;
-  a.ks = static_cast<const uint8_t*>(k->scale);
+  a.ks = k->k_dtype == MXS_K_E4M3 ? nullptr : static_cast<const uint8_t*>(k->scale);
   a.ks_page_stride = k->scale_page_stride;
   a.bt = bt->block_table;
   a.bt_stride = bt->bt_row_stride;

@@ -10,7 +10,8 @@ using namespace dev;
 // Each page is read by exactly one wave, so K goes straight from HBM into
 // registers (staging it in LDS would buy nothing): per 16-token tile, lane
 // (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
-// per wave instruction) and e8m0 byte g of that token. Pages are double-
+// per wave instruction) and e8m0 byte g of that token; from an fp8 cache,
+// bytes 16g..16g+15 and 64+16g..64+16g+15 of the token (2 KB per tile). Pages are double-
 // buffered in registers: the loads of page j+2 are in flight while page j+1
 // is scored. The chunk's page ids are read once into one VGPR (lane l holds
 // the id of page j0 + l) and picked per page with readlane.
@@ -23,31 +24,49 @@ using namespace dev;
 // keeps all chunks of a request on one XCD, whose L2 then serves the
 // request's query and block-table row to every chunk.
 // ---------------------------------------------------------------------------
+// One page in registers. load(): dp/sp are the page's (uniform) bases,
+// doff/soff the lane's byte offsets inside the page (MXFP4 data 64 i + 16 g,
+// scale 4 i + g; fp8 data 128 i + 16 g, whose second slice is 64 bytes on).
+template <int KDT, int P>
+struct RegPage;
+
 template <int P>
-struct RegPage {
+struct RegPage<MXS_K_MXFP4, P> {
   u4 d[P / 16];
   int s[P / 16];
+  static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(i * 64 + 16 * g); }
+  __device__ __forceinline__ KTile<MXS_K_MXFP4> tile(int t) const { return {d[t], s[t]}; }
+  __device__ __forceinline__ void load(const uint8_t* dp, const uint8_t* sp, uint32_t doff, uint32_t soff) {
+#pragma unroll
+    for (int t = 0; t < P / 16; ++t) {
+      d[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 1024u * t));
+      s[t] = __builtin_nontemporal_load(sp + soff + 64u * t);
+    }
+  }
 };
 
-// One page into registers. dp/sp are the page's (uniform) bases; doff/soff the
-// lane's byte offsets inside the page (data: 64 i + 16 g; scale: 4 i + g).
 template <int P>
-__device__ __forceinline__ void load_reg_page(RegPage<P>& kp, const uint8_t* dp, const uint8_t* sp, uint32_t doff,
-                                              uint32_t soff) {
+struct RegPage<MXS_K_E4M3, P> {
+  u4 lo[P / 16];
+  u4 hi[P / 16];
+  static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(i * 128 + 16 * g); }
+  __device__ __forceinline__ KTile<MXS_K_E4M3> tile(int t) const { return {lo[t], hi[t]}; }
+  __device__ __forceinline__ void load(const uint8_t* dp, const uint8_t*, uint32_t doff, uint32_t) {
 #pragma unroll
-  for (int t = 0; t < P / 16; ++t) {
-    kp.d[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 1024u * t));
-    kp.s[t] = __builtin_nontemporal_load(sp + soff + 64u * t);
+    for (int t = 0; t < P / 16; ++t) {
+      lo[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t));
+      hi[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t + 64u));
+    }
   }
-}
+};
 
 // Score one register-resident page against the wave's four query tiles.
 // MASK: the page holds the end of the live window (tokens >= lip are dead).
 // The tile loop is software-pipelined by hand: the four MFMAs of tile t are
 // issued before the results of tile t-1 are folded, and a scheduling fence
 // after each step keeps only two tiles of results live.
-template <int P, bool MASK, bool LG>
-__device__ __forceinline__ void decode_page(const RegPage<P>& kp, const v8i (&qt)[4], int j, int lip, int g,
+template <int KDT, int P, bool MASK, bool LG>
+__device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i (&qt)[4], int j, int lip, int g,
                                             const bool (&hv)[4], float* stage, int jrel, float* lg_row,
                                             const int64_t (&hoff)[4], const KArgs& a) {
   constexpr int TPP = P / 16;
@@ -60,7 +79,7 @@ __device__ __forceinline__ void decode_page(const RegPage<P>& kp, const v8i (&qt
     v4f cur[4];
     if (t < TPP) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) cur[n] = mma_kq(kp.d[t], qt[n], kp.s[t]);
+      for (int n = 0; n < 4; ++n) cur[n] = mma_tile(kp.tile(t), qt[n]);
     }
     if (t > 0) {
       const int tp = t - 1;
@@ -92,7 +111,7 @@ __device__ __forceinline__ void decode_page(const RegPage<P>& kp, const v8i (&qt
   }
 }
 
-template <int QDT, int P, bool LG>
+template <int QDT, int KDT, int P, bool LG>
 __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   constexpr int TPP = P / 16;
   const int lane = threadIdx.x & 63;
@@ -146,21 +165,22 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   float* stage = stage_all[wave];
 
   if (j0 < jl) {
-    const uint32_t doff = (uint32_t)(i * 64 + 16 * g);
+    const uint32_t doff = RegPage<KDT, P>::data_offset(g, i);
     const uint32_t soff = (uint32_t)(i * 4 + g);
-    auto load_page = [&](RegPage<P>& kp, int j) {
+    auto load_page = [&](RegPage<KDT, P>& kp, int j) {
       const int jj = min(j, jl - 1);
       const int64_t page = __builtin_amdgcn_readlane(my_page, jj - j0);
-      load_reg_page<P>(kp, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, doff, soff);
+      kp.load(a.kd + page * a.kd_page_stride, KDT == MXS_K_MXFP4 ? a.ks + page * a.ks_page_stride : nullptr, doff,
+              soff);
     };
-    auto score = [&](const RegPage<P>& kp, int j) {
+    auto score = [&](const RegPage<KDT, P>& kp, int j) {
       const int lip = limit - j * P;                 // live tokens in this page
       if (lip >= P)
-        decode_page<P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+        decode_page<KDT, P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
       else
-        decode_page<P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+        decode_page<KDT, P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
     };
-    RegPage<P> A, B;
+    RegPage<KDT, P> A, B;
     load_page(A, j0);
     load_page(B, j0 + 1);
     // the fences stop the scheduler from hoisting a refill above the scoring
@@ -212,31 +232,29 @@ int occ_of(K kernel) {
   return n > 0 ? n : 1;
 }
 
-template <int QDT, int P>
-hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<KArgs*>(&a)};
-  const void* fn = a.lg ? reinterpret_cast<const void*>(&k_decode<QDT, P, true>)
-                        : reinterpret_cast<const void*>(&k_decode<QDT, P, false>);
-  return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
-}
+template <int QDT, int KDT, int P>
+struct Launch {
+  static hipError_t run(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    const void* fn = a.lg ? reinterpret_cast<const void*>(&k_decode<QDT, KDT, P, true>)
+                          : reinterpret_cast<const void*>(&k_decode<QDT, KDT, P, false>);
+    return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+  }
+};
+
+template <int QDT, int KDT, int P>
+struct Occupancy {
+  static int run(bool lg) { return lg ? occ_of(&k_decode<QDT, KDT, P, true>) : occ_of(&k_decode<QDT, KDT, P, false>); }
+};
 
 }  // namespace
 
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  if (plan.q_dtype == MXS_Q_BF16)
-    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
-  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+  return dispatch_variant<Launch>(plan.q_dtype, plan.k_dtype, plan.page_size, plan, a, stream);
 }
 
-template <int QDT, int P>
-int occ_qp(bool lg) {
-  return lg ? occ_of(&k_decode<QDT, P, true>) : occ_of(&k_decode<QDT, P, false>);
-}
-
-int occupancy_decode(int32_t q_dtype, int32_t page_size, bool want_lg) {
-  if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_qp<MXS_Q_BF16, 128>(want_lg) : occ_qp<MXS_Q_BF16, 64>(want_lg);
-  return page_size == 128 ? occ_qp<MXS_Q_E4M3, 128>(want_lg) : occ_qp<MXS_Q_E4M3, 64>(want_lg);
+int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_lg) {
+  return dispatch_variant<Occupancy>(q_dtype, k_dtype, page_size, want_lg);
 }
 
 }  // namespace mxs

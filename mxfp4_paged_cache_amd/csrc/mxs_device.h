@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 scorer kernels (mxs_decode.hip,
-// mxs_prefill.hip). Not part of the public ABI.
+// mxs_prefill.hip, mxs_logits.hip) and the writer. Not part of the public ABI.
 //
 // One instruction does the arithmetic: v_mfma_scale_f32_16x16x128_f8f6f4
 // with the MXFP4 K tile as the fp4 operand, the e4m3 query tile as the fp8
@@ -141,38 +141,105 @@ __device__ __forceinline__ void store_logits4(float* row, int t0, v4f v, int W, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// K formats. MXFP4 (MXS_K_MXFP4): 64 data bytes + 4 e8m0 bytes per token, the
+// fp4 operand as stored. fp8 (MXS_K_E4M3, the cache the MXFP4 one replaces,
+// aiter #7061, "Summary"): 128 e4m3 bytes per token, fed as the fp8 operand
+// in the query's element layout (bytes 16g..16g+15 and 64+16g..64+16g+15 of
+// the token for lane group g), both scales 127 (x1).
+// ---------------------------------------------------------------------------
+template <int KDT>
+struct KTile;
+template <>
+struct KTile<MXS_K_MXFP4> {
+  u4 d;    // elements 32g..32g+31 of token i (16 bytes)
+  int s;   // their e8m0 byte
+};
+template <>
+struct KTile<MXS_K_E4M3> {
+  u4 lo;   // elements 16g..16g+15
+  u4 hi;   // elements 64+16g..64+16g+15
+};
+
+__device__ __forceinline__ v4f mma_tile(const KTile<MXS_K_MXFP4>& k, v8i q) { return mma_kq(k.d, q, k.s); }
+
+__device__ __forceinline__ v4f mma_tile(const KTile<MXS_K_E4M3>& k, v8i q) {
+  const v8i a = {(int)k.lo[0], (int)k.lo[1], (int)k.lo[2], (int)k.lo[3],
+                 (int)k.hi[0], (int)k.hi[1], (int)k.hi[2], (int)k.hi[3]};
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q, z, 0, 0, 0, 127, 0, 127);
+}
+
+// Bytes of one page staged in LDS.
+template <int KDT, int P>
+constexpr int kStagedPageBytes = KDT == MXS_K_E4M3 ? P * 128 : P * 68;
+
+// LDS layout of a staged page. MXFP4: the data of 16-token tile t is stored
+// as [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16
+// lanes of a group read 256 contiguous bytes (no bank conflicts on
+// ds_read_b128); the scales follow as [token][4 bytes] at P * 64. fp8: tile t
+// is [half h][g][i][16 bytes] at 2048 t + 1024 h + 256 g + 16 i, half h
+// holding bytes 64 h + 16 g .. + 15 of token 16 t + i.
+template <int KDT, int P>
+__device__ __forceinline__ KTile<KDT> lds_tile(const uint8_t* kb, int g, int i, int t) {
+  KTile<KDT> r;
+  if constexpr (KDT == MXS_K_E4M3) {
+    r.lo = *reinterpret_cast<const u4*>(kb + 2048 * t + 256 * g + 16 * i);
+    r.hi = *reinterpret_cast<const u4*>(kb + 2048 * t + 1024 + 256 * g + 16 * i);
+  } else {
+    r.d = *reinterpret_cast<const u4*>(kb + 1024 * t + 256 * g + 16 * i);
+    r.s = kb[P * 64 + 64 * t + 4 * i + g];
+  }
+  return r;
+}
+
 // One page of K staged through registers into LDS by a whole workgroup.
-template <int P>
+template <int KDT, int P>
 struct PageStage {
-  static constexpr int kDataChunks = P * 64 / 16 / kThreads;   // 16-byte chunks per thread
+  static constexpr int kDataChunks = P * (KDT == MXS_K_E4M3 ? 128 : 64) / 16 / kThreads;   // 16-byte chunks per thread
   u4 d[kDataChunks];
   uint32_t sc;
 };
 
-// LDS layout of a staged page: the data of 16-token tile t is stored as
-// [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16 lanes of
-// a group read 256 contiguous bytes (no bank conflicts on ds_read_b128); the
-// scales follow as [token][4 bytes] at P * 64. Thread tid fills LDS slot
-// s = tid + 256 c (16 bytes, contiguous writes) with global bytes
-// 16 g..16 g+15 of token 16 t + i, (t, g, i) = (s / 64, s / 16 % 4, s % 16):
-// a wave still loads one contiguous 1 KB tile per instruction.
-template <int P>
-__device__ __forceinline__ void stage_load(PageStage<P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
+// MXFP4: thread tid fills LDS slot s = tid + 256 c (16 bytes, contiguous
+// writes) with global bytes 16 g..16 g+15 of token 16 t + i, (t, g, i) =
+// (s / 64, s / 16 % 4, s % 16): a wave still loads one contiguous 1 KB tile
+// per instruction. fp8: thread tid loads global chunk s (bytes 16 s..16 s+15
+// of the page: token s / 8, half (s / 4) % 2, group s % 4), so a wave loads
+// 1 KB contiguously, and stores it at its place in the tile layout.
+template <int KDT, int P>
+__device__ __forceinline__ void stage_load(PageStage<KDT, P>& st, const uint8_t* dp, const uint8_t* sp, int tid) {
 #pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c) {
+  for (int c = 0; c < PageStage<KDT, P>::kDataChunks; ++c) {
     const int sl = tid + kThreads * c;
-    const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
-    st.d[c] = *reinterpret_cast<const u4*>(dp + off);
+    if constexpr (KDT == MXS_K_E4M3) {
+      st.d[c] = *reinterpret_cast<const u4*>(dp + 16 * sl);
+    } else {
+      const int off = ((sl >> 6) * 16 + (sl & 15)) * 64 + ((sl >> 4) & 3) * 16;
+      st.d[c] = *reinterpret_cast<const u4*>(dp + off);
+    }
   }
-  if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+  if constexpr (KDT == MXS_K_MXFP4) {
+    if (tid < P) st.sc = *reinterpret_cast<const uint32_t*>(sp + 4 * tid);
+  }
 }
 
-template <int P>
-__device__ __forceinline__ void stage_store(const PageStage<P>& st, uint8_t* buf, int tid) {
+template <int KDT, int P>
+__device__ __forceinline__ void stage_store(const PageStage<KDT, P>& st, uint8_t* buf, int tid) {
 #pragma unroll
-  for (int c = 0; c < PageStage<P>::kDataChunks; ++c)
-    *reinterpret_cast<u4*>(buf + 16 * (tid + kThreads * c)) = st.d[c];
-  if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
+  for (int c = 0; c < PageStage<KDT, P>::kDataChunks; ++c) {
+    const int sl = tid + kThreads * c;
+    if constexpr (KDT == MXS_K_E4M3) {
+      const int tok = sl >> 3, c8 = sl & 7;
+      const int at = (tok >> 4) * 2048 + (c8 >> 2) * 1024 + (c8 & 3) * 256 + (tok & 15) * 16;
+      *reinterpret_cast<u4*>(buf + at) = st.d[c];
+    } else {
+      *reinterpret_cast<u4*>(buf + 16 * sl) = st.d[c];
+    }
+  }
+  if constexpr (KDT == MXS_K_MXFP4) {
+    if (tid < P) *reinterpret_cast<uint32_t*>(buf + P * 64 + 4 * tid) = st.sc;
+  }
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -1,6 +1,6 @@
 // Internal interface between the host entry points (mxs_api.cpp) and the
-// gfx950 kernels (mxs_decode.hip, mxs_prefill.hip, mxs_logits.hip). Not part
-// of the public ABI.
+// gfx950 kernels (mxs_decode.hip, mxs_prefill.hip, mxs_logits.hip,
+// mxs_select.hip, mxs_write.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,7 +38,7 @@ struct KArgs {
   int32_t H;
   const uint8_t* kd;
   int64_t kd_page_stride;   // bytes
-  const uint8_t* ks;
+  const uint8_t* ks;        // e8m0 scales (MXFP4 cache; null for an fp8 cache)
   int64_t ks_page_stride;   // bytes
   const int32_t* bt;
   int64_t bt_stride;        // elements
@@ -95,10 +95,11 @@ struct WArgs {
   int64_t n;
   uint8_t* kd;
   int64_t kd_page_stride;   // bytes
-  uint8_t* ks;
+  uint8_t* ks;              // MXFP4 only
   int64_t ks_page_stride;   // bytes
   int64_t num_pages;
   int32_t P;
+  int32_t kdt;              // MXS_K_MXFP4 or MXS_K_E4M3
 };
 
 // Launchers. Return the HIP status of the launch.
@@ -108,10 +109,10 @@ hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t strea
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 
-// Workgroups of the kernel variant (q dtype, page size, outputs) that fit on one CU.
-int occupancy_decode(int32_t q_dtype, int32_t page_size, bool want_lg);
-int occupancy_prefill(int32_t q_dtype, int32_t page_size);
-int occupancy_logits(int32_t q_dtype, int32_t page_size, bool want_bs);
+// Workgroups of the kernel variant (q dtype, cache dtype, page size, outputs) that fit on one CU.
+int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_lg);
+int occupancy_prefill(int32_t q_dtype, int32_t k_dtype, int32_t page_size);
+int occupancy_logits(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs);
 
 inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
   return plan.kernel == KID_DECODE    ? launch_decode(plan, a, stream)
@@ -119,10 +120,23 @@ inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t strea
                                       : launch_logits(plan, a, stream);
 }
 
-inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t page_size, bool want_bs, bool want_lg) {
-  return kernel == KID_DECODE    ? occupancy_decode(q_dtype, page_size, want_lg)
-         : kernel == KID_PREFILL ? occupancy_prefill(q_dtype, page_size)
-                                 : occupancy_logits(q_dtype, page_size, want_bs);
+inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs, bool want_lg) {
+  return kernel == KID_DECODE    ? occupancy_decode(q_dtype, k_dtype, page_size, want_lg)
+         : kernel == KID_PREFILL ? occupancy_prefill(q_dtype, k_dtype, page_size)
+                                 : occupancy_logits(q_dtype, k_dtype, page_size, want_bs);
+}
+
+// F<QDT, KDT, P>::run(args...) for one (query dtype, cache dtype, page size).
+template <template <int, int, int> class F, typename... Args>
+inline auto dispatch_variant(int32_t q_dtype, int32_t k_dtype, int32_t page_size, Args&&... args) {
+  if (q_dtype == MXS_Q_BF16) {
+    if (k_dtype == MXS_K_E4M3)
+      return page_size == 128 ? F<MXS_Q_BF16, MXS_K_E4M3, 128>::run(args...) : F<MXS_Q_BF16, MXS_K_E4M3, 64>::run(args...);
+    return page_size == 128 ? F<MXS_Q_BF16, MXS_K_MXFP4, 128>::run(args...) : F<MXS_Q_BF16, MXS_K_MXFP4, 64>::run(args...);
+  }
+  if (k_dtype == MXS_K_E4M3)
+    return page_size == 128 ? F<MXS_Q_E4M3, MXS_K_E4M3, 128>::run(args...) : F<MXS_Q_E4M3, MXS_K_E4M3, 64>::run(args...);
+  return page_size == 128 ? F<MXS_Q_E4M3, MXS_K_MXFP4, 128>::run(args...) : F<MXS_Q_E4M3, MXS_K_MXFP4, 64>::run(args...);
 }
 
 }  // namespace mxs

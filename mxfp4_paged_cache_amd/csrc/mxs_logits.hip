@@ -11,8 +11,8 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // One workgroup per work item (request, block of 64 query slots, chunk of
 // pages), looping over items with a grid stride; each wave holds one 16-slot
-// query tile. A page is staged once per workgroup in LDS (as in prefill) and
-// multiplied by all four waves.
+// query tile. A page is staged once per workgroup in LDS (as in prefill, for
+// either cache format) and multiplied by all four waves.
 //
 // The output dominates this path (4 bytes per (row, head, token)), so it is
 // written the way HBM takes it fastest: the MFMA results of each wave go
@@ -30,9 +30,9 @@ constexpr int kLogitsSlots = kWaves * 16;   // query slots per work item
 constexpr int kWinTokens = 128;             // tokens per output window: 512 bytes of a logits row
 constexpr int kWinPitch = kWinTokens + 4;   // LDS row pitch in floats (16-byte pad: no bank conflicts)
 
-template <int QDT, int P, bool WANT_BS>
+template <int QDT, int KDT, int P, bool WANT_BS>
 __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
-  constexpr int PB = P * 68;               // bytes of one staged page
+  constexpr int PB = kStagedPageBytes<KDT, P>;   // bytes of one staged page
   constexpr int TPP = P / 16;              // 16-token tiles per page
   constexpr int PPW = kWinTokens / P;      // pages per output window
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
@@ -99,11 +99,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     // page ids, 64 at a time: lane l holds the id of page jid + l
     int jid = j0;
     int ids = (j0 + lane < jl) ? btrow[j0 + lane] : 0;
+    auto load_page = [&](PageStage<KDT, P>& st, int64_t page) {
+      stage_load<KDT, P>(st, a.kd + page * a.kd_page_stride,
+                         KDT == MXS_K_MXFP4 ? a.ks + page * a.ks_page_stride : nullptr, tid);
+    };
     if (j0 < jl) {
-      PageStage<P> st;
-      const int64_t page = __builtin_amdgcn_readfirstlane(ids);
-      stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
-      stage_store<P>(st, kbuf, tid);
+      PageStage<KDT, P> st;
+      load_page(st, __builtin_amdgcn_readfirstlane(ids));
+      stage_store<KDT, P>(st, kbuf, tid);
     }
     __syncthreads();
     for (int j = j0; j < j1; ++j) {
@@ -112,25 +115,22 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
       bool scored = false;
       if (j < jl) {
         const bool more = j + 1 < jl;
-        PageStage<P> nx;
+        PageStage<KDT, P> nx;
         if (more) {
           if (j + 1 - jid == 64) {
             jid += 64;
             ids = (jid + lane < jl) ? btrow[jid + lane] : 0;
           }
-          const int64_t page = __builtin_amdgcn_readlane(ids, j + 1 - jid);
-          stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+          load_page(nx, __builtin_amdgcn_readlane(ids, j + 1 - jid));
         }
         if (j * P < wave_max_lim) {   // some slot of this wave sees the page
           scored = true;
           const uint8_t* kb = kbuf + ((j - j0) & 1) * PB;
-          const uint8_t* kdl = kb + g * 256 + i * 16;
-          const uint8_t* ksl = kb + P * 64 + i * 4 + g;
           const int lrel = lim - j * P - 4 * g;
           const bool mask = (j + 1) * P > wave_min_lim;
 #pragma unroll
           for (int t = 0; t < TPP; ++t) {
-            v4f c = mma_kq(*reinterpret_cast<const u4*>(kdl + 1024 * t), qt, ksl[64 * t]);
+            v4f c = mma_tile(lds_tile<KDT, P>(kb, g, i, t), qt);
             if (mask) {
 #pragma unroll
               for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel) ? c[v] : kNegInf;
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
             *reinterpret_cast<v4f*>(wcolp + 16 * t) = c * s;
           }
         }
-        if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
+        if (more) stage_store<KDT, P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
       }
       if (!scored) {
 #pragma unroll
@@ -181,31 +181,29 @@ int occ_of(K kernel) {
   return n > 0 ? n : 1;
 }
 
-template <int QDT, int P>
-hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<KArgs*>(&a)};
-  const void* fn = a.bs ? reinterpret_cast<const void*>(&k_logits<QDT, P, true>)
-                        : reinterpret_cast<const void*>(&k_logits<QDT, P, false>);
-  return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
-}
+template <int QDT, int KDT, int P>
+struct Launch {
+  static hipError_t run(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    const void* fn = a.bs ? reinterpret_cast<const void*>(&k_logits<QDT, KDT, P, true>)
+                          : reinterpret_cast<const void*>(&k_logits<QDT, KDT, P, false>);
+    return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+  }
+};
 
-template <int QDT, int P>
-int occ_qp(bool bs) {
-  return bs ? occ_of(&k_logits<QDT, P, true>) : occ_of(&k_logits<QDT, P, false>);
-}
+template <int QDT, int KDT, int P>
+struct Occupancy {
+  static int run(bool bs) { return bs ? occ_of(&k_logits<QDT, KDT, P, true>) : occ_of(&k_logits<QDT, KDT, P, false>); }
+};
 
 }  // namespace
 
 hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  if (plan.q_dtype == MXS_Q_BF16)
-    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
-  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+  return dispatch_variant<Launch>(plan.q_dtype, plan.k_dtype, plan.page_size, plan, a, stream);
 }
 
-int occupancy_logits(int32_t q_dtype, int32_t page_size, bool want_bs) {
-  if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_qp<MXS_Q_BF16, 128>(want_bs) : occ_qp<MXS_Q_BF16, 64>(want_bs);
-  return page_size == 128 ? occ_qp<MXS_Q_E4M3, 128>(want_bs) : occ_qp<MXS_Q_E4M3, 64>(want_bs);
+int occupancy_logits(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs) {
+  return dispatch_variant<Occupancy>(q_dtype, k_dtype, page_size, want_bs);
 }
 
 }  // namespace mxs

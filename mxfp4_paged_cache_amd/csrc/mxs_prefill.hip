@@ -13,8 +13,8 @@ using namespace dev;
 // query slot is (row, head); slot = row * H + head, so a 16-slot tile is 16
 // heads of one row when H is a multiple of 16. Each wave keeps 8 query tiles
 // in registers for the whole item; every page is staged once per workgroup in
-// LDS (double-buffered, 8.5 KB per buffer at P = 128) and read by all four
-// waves. Block scores are staged in LDS for up to 16 pages and leave as
+// LDS (double-buffered, 8.5 KB per buffer at P = 128 for MXFP4, 16 KB for an
+// fp8 cache) and read by all four waves. Block scores are staged in LDS for up to 16 pages and leave as
 // contiguous per-slot rows.
 //
 // Work items are ordered slot block fastest: at any moment the whole grid
@@ -32,18 +32,16 @@ constexpr int kFlushLanesPerRow = kPrefillStagePages / 4;     // 4 pages per lan
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
 // The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
 // most two tiles of MFMA results are live.
-template <int P, int NQ, bool MASK>
+template <int KDT, int P, int NQ, bool MASK>
 __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[NQ], const int (&lrel)[NQ], int g,
                                              int i, float (&r)[NQ]) {
   constexpr int TPP = P / 16;
-  const uint8_t* kdl = kb + g * 256 + i * 16;     // this lane's 16 bytes of tile t: kdl + 1024 t
-  const uint8_t* ksl = kb + P * 64 + i * 4 + g;   // this lane's scale byte of tile t: ksl + 64 t
   float m[NQ];
 #pragma unroll
   for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
-  auto mma = [&](u4 k, int sc, v4f (&c)[NQ]) {
+  auto mma = [&](const KTile<KDT>& k, v4f (&c)[NQ]) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) c[n] = mma_kq(k, qt[n], sc);
+    for (int n = 0; n < NQ; ++n) c[n] = mma_tile(k, qt[n]);
   };
   auto fold = [&](int t, const v4f (&cc)[NQ]) {
 #pragma unroll
@@ -58,20 +56,16 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
   };
   // two tiles per trip, no MFMA result carried across trips; the next pair of
   // K tiles is read from LDS while this pair is multiplied and folded
-  u4 k0 = *reinterpret_cast<const u4*>(kdl);
-  int s0 = ksl[0];
-  u4 k1 = *reinterpret_cast<const u4*>(kdl + 1024);
-  int s1 = ksl[64];
+  KTile<KDT> k0 = lds_tile<KDT, P>(kb, g, i, 0);
+  KTile<KDT> k1 = lds_tile<KDT, P>(kb, g, i, 1);
 #pragma unroll 1
   for (int t = 0; t < TPP; t += 2) {
     v4f cA[NQ], cB[NQ];
-    mma(k0, s0, cA);
-    mma(k1, s1, cB);
+    mma(k0, cA);
+    mma(k1, cB);
     if (t + 2 < TPP) {
-      k0 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 2));
-      s0 = ksl[64 * (t + 2)];
-      k1 = *reinterpret_cast<const u4*>(kdl + 1024 * (t + 3));
-      s1 = ksl[64 * (t + 3)];
+      k0 = lds_tile<KDT, P>(kb, g, i, t + 2);
+      k1 = lds_tile<KDT, P>(kb, g, i, t + 3);
     }
     fold(t, cA);
     fold(t + 1, cB);
@@ -80,10 +74,10 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
   for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
 }
 
-template <int QDT, int P>
+template <int QDT, int KDT, int P>
 __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
   constexpr int NQ = kPrefillTiles;
-  constexpr int PB = P * 68;   // bytes of one staged page
+  constexpr int PB = kStagedPageBytes<KDT, P>;   // bytes of one staged page
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
   __shared__ float stage[kPrefillSlots * kPrefillStageStride];
   const int tid = threadIdx.x;
@@ -133,11 +127,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     // a table read before its loads can issue)
     int jid = j0;
     int ids = (j0 + lane < jl) ? btrow[j0 + lane] : 0;
+    auto load_page = [&](PageStage<KDT, P>& st, int64_t page) {
+      stage_load<KDT, P>(st, a.kd + page * a.kd_page_stride,
+                         KDT == MXS_K_MXFP4 ? a.ks + page * a.ks_page_stride : nullptr, tid);
+    };
     if (j0 < jl) {
-      PageStage<P> st;
-      const int64_t page = __builtin_amdgcn_readfirstlane(ids);
-      stage_load<P>(st, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
-      stage_store<P>(st, kbuf, tid);
+      PageStage<KDT, P> st;
+      load_page(st, __builtin_amdgcn_readfirstlane(ids));
+      stage_store<KDT, P>(st, kbuf, tid);
     }
     __syncthreads();
     int jbase = j0;
@@ -145,24 +142,23 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       float r[NQ];
       if (j < jl) {
         const bool more = j + 1 < jl;
-        PageStage<P> nx;
+        PageStage<KDT, P> nx;
         if (more) {
           if (j + 1 - jid == 64) {
             jid += 64;
             ids = (jid + lane < jl) ? btrow[jid + lane] : 0;
           }
-          const int64_t page = __builtin_amdgcn_readlane(ids, j + 1 - jid);
-          stage_load<P>(nx, a.kd + page * a.kd_page_stride, a.ks + page * a.ks_page_stride, tid);
+          load_page(nx, __builtin_amdgcn_readlane(ids, j + 1 - jid));
         }
         const uint8_t* kb = kbuf + ((j - j0) & 1) * PB;
         int lrel[NQ];
 #pragma unroll
         for (int n = 0; n < NQ; ++n) lrel[n] = lim[n] - j * P - 4 * g;
         if ((j + 1) * P > wave_min_lim)
-          prefill_page<P, NQ, true>(kb, qt, lrel, g, i, r);
+          prefill_page<KDT, P, NQ, true>(kb, qt, lrel, g, i, r);
         else
-          prefill_page<P, NQ, false>(kb, qt, lrel, g, i, r);
-        if (more) stage_store<P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
+          prefill_page<KDT, P, NQ, false>(kb, qt, lrel, g, i, r);
+        if (more) stage_store<KDT, P>(nx, kbuf + ((j + 1 - j0) & 1) * PB, tid);
       } else {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) r[n] = kNegInf;
@@ -228,25 +224,28 @@ int occ_of(K kernel) {
   return n > 0 ? n : 1;
 }
 
-template <int QDT, int P>
-hipError_t launch_qp(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<KArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&k_prefill<QDT, P>), dim3(plan.grid), dim3(kThreads), args, 0,
-                         stream);
-}
+template <int QDT, int KDT, int P>
+struct Launch {
+  static hipError_t run(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_prefill<QDT, KDT, P>), dim3(plan.grid), dim3(kThreads),
+                           args, 0, stream);
+  }
+};
+
+template <int QDT, int KDT, int P>
+struct Occupancy {
+  static int run() { return occ_of(&k_prefill<QDT, KDT, P>); }
+};
 
 }  // namespace
 
 hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
-  if (plan.q_dtype == MXS_Q_BF16)
-    return plan.page_size == 128 ? launch_qp<MXS_Q_BF16, 128>(plan, a, stream) : launch_qp<MXS_Q_BF16, 64>(plan, a, stream);
-  return plan.page_size == 128 ? launch_qp<MXS_Q_E4M3, 128>(plan, a, stream) : launch_qp<MXS_Q_E4M3, 64>(plan, a, stream);
+  return dispatch_variant<Launch>(plan.q_dtype, plan.k_dtype, plan.page_size, plan, a, stream);
 }
 
-int occupancy_prefill(int32_t q_dtype, int32_t page_size) {
-  if (q_dtype == MXS_Q_BF16)
-    return page_size == 128 ? occ_of(&k_prefill<MXS_Q_BF16, 128>) : occ_of(&k_prefill<MXS_Q_BF16, 64>);
-  return page_size == 128 ? occ_of(&k_prefill<MXS_Q_E4M3, 128>) : occ_of(&k_prefill<MXS_Q_E4M3, 64>);
+int occupancy_prefill(int32_t q_dtype, int32_t k_dtype, int32_t page_size) {
+  return dispatch_variant<Occupancy>(q_dtype, k_dtype, page_size);
 }
 
 }  // namespace mxs

@@ -6,6 +6,9 @@
 //   e = floor(log2(amax)) - 2 per 32-element block, stored as byte e + 127
 //   clipped to [1, 254]; each element is the e2m1 value nearest to x / 2^e,
 //   ties to the even code, saturated at 6, sign kept.
+// An fp8 cache (the format the MXFP4 one replaces, aiter #7061, "Summary")
+// gets each element as the nearest e4m3 value (ties to even, saturated at
+// +-448, unit scale), the rounding the query takes.
 #include "mxs_device.h"
 
 namespace mxs {
@@ -26,6 +29,7 @@ using namespace dev;
 // all loads first, so that enough bytes are in flight to cover the latency.
 constexpr int kWriteSteps = 4;
 
+template <int KDT>
 __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
   const int lane = threadIdx.x & 63;
   const int sub = lane >> 4, l = lane & 15;
@@ -49,6 +53,15 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
 #pragma unroll
     for (int u = 0; u < kWriteSteps; ++u) {
       const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      if constexpr (KDT == MXS_K_E4M3) {
+        // fp8 cache: elements 8 l .. 8 l + 7 as e4m3 bytes, in element order
+        const uint2 v = {(uint32_t)bf16x4_to_e4m3(w4[0], w4[1]), (uint32_t)bf16x4_to_e4m3(w4[2], w4[3])};
+        if (ok[u]) {
+          const int64_t off = slot[u] - page[u] * a.P;
+          *reinterpret_cast<uint2*>(a.kd + page[u] * a.kd_page_stride + off * 128 + 8 * l) = v;
+        }
+        continue;
+      }
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -83,8 +96,9 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
 
 hipError_t launch_write(int64_t grid, const WArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<WArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&k_write), dim3((uint32_t)grid), dim3(kThreads), args, 0,
-                         stream);
+  const void* fn = a.kdt == MXS_K_E4M3 ? reinterpret_cast<const void*>(&k_write<MXS_K_E4M3>)
+                                       : reinterpret_cast<const void*>(&k_write<MXS_K_MXFP4>);
+  return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace mxs

@@ -11,6 +11,8 @@ Recipe (the pages' scorer benchmarks use random K data with e8m0 bytes in
 * K data: uniform random bytes, so both e2m1 codes of a byte are uniform over
   all 16 codes;
 * K scales: uniform random e8m0 bytes in [lo, hi] per (token, 32-element block);
+* fp8 cache (k_dtype "e4m3", the format the MXFP4 one replaces): 128 bytes
+  per token drawn uniformly over the 254 finite e4m3 codes, no scale view;
 * block table: distinct pages drawn without replacement from a larger pool, so
   the gather is a real random gather;
 * cu_seqlens_q / seq_lens / prefix_lens: as the workload states.
@@ -57,6 +59,7 @@ class Workload:
     tables: int = 1                 # disjoint block tables (benchmark rotation)
     select_k: int = 0               # > 0: the workload is top-k page selection over this prefill's block scores
     write_tokens: int = 0           # > 0: the workload is writing this many bf16 keys into page slots
+    k_dtype: str = "mxfp4"          # "mxfp4" (e2m1 + e8m0 views) | "e4m3" (fp8 cache, 128 B per token)
     note: str = ""
 
     @property
@@ -104,8 +107,8 @@ def _gen(seed: int, fid: int, device) -> torch.Generator:
 class Inputs:
     wl: Workload
     q: torch.Tensor                 # [T, H, 128] bf16 or float8_e4m3fn (may be a strided view)
-    k_data: torch.Tensor            # uint8 view [pages, P, 64]
-    k_scale: torch.Tensor           # uint8 view [pages, P, 4]
+    k_data: torch.Tensor            # uint8 view [pages, P, 64] (fp8 cache: [pages, P, 128])
+    k_scale: Optional[torch.Tensor]  # uint8 view [pages, P, 4] (fp8 cache: None)
     block_tables: List[torch.Tensor]  # int32 [B, width], one per rotation
     cu_seqlens_q: torch.Tensor      # int32 [B+1]
     seq_lens: torch.Tensor          # int32 [B]
@@ -146,15 +149,26 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
     gt = _gen(seed, F_TABLE, "cpu")
 
     region = None
+    fp8 = wl.k_dtype == "e4m3"
+    tb = 128 if fp8 else SLOT_DATA_BYTES     # data bytes per token
+    sb = 0 if fp8 else SLOT_SCALE_BYTES      # scale bytes per token
+
+    def data_bytes(shape):
+        if not fp8:
+            return torch.randint(0, 256, shape, generator=gd, device=device, dtype=torch.uint8)
+        # uniform over the 254 finite e4m3 codes: skip 0x7F (and 0xFF, never drawn)
+        u = torch.randint(0, 254, shape, generator=gd, device=device, dtype=torch.uint8)
+        return u + (u >= 0x7F).to(torch.uint8)
+
     if wl.layout == "split":
-        k_data = torch.randint(0, 256, (pool, P, SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
-        k_scale = torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, P, SLOT_SCALE_BYTES), generator=gs,
-                                device=device, dtype=torch.uint8)
+        k_data = data_bytes((pool, P, tb))
+        k_scale = None if fp8 else torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, P, SLOT_SCALE_BYTES),
+                                                 generator=gs, device=device, dtype=torch.uint8)
     else:
         # One uint8 region. "region": page = [P x 64 B data][P x 4 B scale].
         # "shared": page block = two layer slots of that shape; slot 1 is scored,
         # every byte outside the scored pages is 0xFF (e2m1 -6, e8m0 NaN).
-        slot = P * (SLOT_DATA_BYTES + SLOT_SCALE_BYTES)
+        slot = P * (tb + sb)
         stride = slot if wl.layout == "region" else 2 * slot
         off = 0 if wl.layout == "region" else slot
         region = torch.full((pool * stride,), 0xFF, device=device, dtype=torch.uint8)
@@ -162,14 +176,15 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
         lo = wl.shared_first_page if wl.layout == "shared" else 0
         hi = pool
         nused = hi - lo
-        data_part = torch.randint(0, 256, (nused, P * SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
-        scale_part = torch.randint(wl.scale_lo, wl.scale_hi + 1, (nused, P * SLOT_SCALE_BYTES), generator=gs,
-                                   device=device, dtype=torch.uint8)
-        view[lo:hi, off:off + P * SLOT_DATA_BYTES] = data_part
-        view[lo:hi, off + P * SLOT_DATA_BYTES:off + slot] = scale_part
-        k_data = torch.as_strided(region, (pool, P, SLOT_DATA_BYTES), (stride, SLOT_DATA_BYTES, 1), off)
-        k_scale = torch.as_strided(region, (pool, P, SLOT_SCALE_BYTES), (stride, SLOT_SCALE_BYTES, 1),
-                                   off + P * SLOT_DATA_BYTES)
+        view[lo:hi, off:off + P * tb] = data_bytes((nused, P * tb))
+        k_data = torch.as_strided(region, (pool, P, tb), (stride, tb, 1), off)
+        k_scale = None
+        if not fp8:
+            scale_part = torch.randint(wl.scale_lo, wl.scale_hi + 1, (nused, P * SLOT_SCALE_BYTES), generator=gs,
+                                       device=device, dtype=torch.uint8)
+            view[lo:hi, off + P * tb:off + slot] = scale_part
+            k_scale = torch.as_strided(region, (pool, P, SLOT_SCALE_BYTES), (stride, SLOT_SCALE_BYTES, 1),
+                                       off + P * tb)
 
     # block tables: distinct pages; rotations use disjoint page sets
     lo = wl.shared_first_page if wl.layout == "shared" else 0
@@ -251,6 +266,30 @@ def write_1m_tokens() -> Workload:
                     seq_lens=[1], pool_pages=300_000, write_tokens=1 << 20)
 
 
+def decode_b64_128k_fp8() -> Workload:
+    """The decode workload over an fp8 (e4m3, 128 B per token) index cache: the format the MXFP4 one replaces."""
+    wl = decode_b64_128k()
+    wl.name = "decode_b64_ctx128k_fp8cache"
+    wl.k_dtype = "e4m3"
+    return wl
+
+
+def prefill_long_fp8() -> Workload:
+    """The 4096-row, 128K-context prefill over an fp8 index cache."""
+    wl = prefill_long()
+    wl.name = "prefill_q4096_ctx128k_fp8cache"
+    wl.k_dtype = "e4m3"
+    return wl
+
+
+def write_1m_tokens_fp8() -> Workload:
+    """Writing 1,048,576 bf16 keys into an fp8 index cache (128 e4m3 bytes per token)."""
+    wl = write_1m_tokens()
+    wl.name = "write_1m_tokens_p128_fp8cache"
+    wl.k_dtype = "e4m3"
+    return wl
+
+
 CONFIGS = {
     1: prefill_small,
     2: decode_b64_128k,
@@ -259,4 +298,7 @@ CONFIGS = {
     5: logits_shared_pool,
     6: select_after_prefill_long,
     7: write_1m_tokens,
+    8: decode_b64_128k_fp8,
+    9: prefill_long_fp8,
+    10: write_1m_tokens_fp8,
 }

@@ -19,6 +19,11 @@ A token t goes to slot slot_mapping[t] = page * P + offset (-1: skipped):
 data bytes at page * data_page_stride + offset * 64, scale bytes at
 page * scale_page_stride + offset * 4; element 2m in the low nibble of
 byte m (the layout the scorer reads).
+
+An fp8 index cache (the format the MXFP4 one replaces; aiter #7061,
+"Summary": 128 B of e4m3 per token) gets each element as the nearest e4m3
+value, ties to the even code, saturated at +-448, unit scale -- the rounding
+the query takes (aiter #7061, "Kernels") -- at byte offset * 128 + e.
 """
 from __future__ import annotations
 
@@ -70,6 +75,17 @@ def quantize_token(bits) -> tuple:
             i = 32 * k + e
             data[i // 2] |= c << (4 * (i % 2))
     return bytes(data), bytes(scales)
+
+
+def write_pages_e4m3(k_bits: np.ndarray, slot_mapping, k_data: np.ndarray, page_size: int) -> None:
+    """Round k_bits [N, 128] (uint16 bf16 patterns) to e4m3 bytes into the fp8
+    page view k_data [pages, P, 128] (uint8), in place; slot -1 skips."""
+    from oracle import bf16_to_e4m3
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        page, off = divmod(int(slot), page_size)
+        k_data[page, off, :] = [bf16_to_e4m3(int(b)) for b in k_bits[t]]
 
 
 def write_pages(k_bits: np.ndarray, slot_mapping, k_data: np.ndarray, k_scale: np.ndarray, page_size: int) -> None:

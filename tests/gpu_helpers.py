@@ -13,6 +13,14 @@ output indexing and the argmax over pages must match exactly (the argmax
 may differ only between values that are equal within the same bound).
 A floor on the fraction of bit-identical values guards against systematic
 drift that the per-element bound would let through.
+
+An fp8 (e4m3) cache runs the same instruction with both operands e4m3. Its
+products carry 8 significant bits and, with K spread over all e4m3 codes,
+span about 2^17 within a group, so the group truncation shows on most values
+(measured on gfx950: 0.05% bit-identical for uniform codes, 23% for e4m3 of
+N(0, 1); err / (sm_scale * M) at most 2^-13.1, 99th percentile 2^-14.6).
+The per-element bound is unchanged; in place of the bit-identical floor the
+99th percentile of err / (sm_scale * M) must stay below 2^-12.
 """
 from __future__ import annotations
 
@@ -66,14 +74,17 @@ def oracle_run(inp: W.Inputs, *, rows=None, want_logits=True, want_blocks=True, 
         used = np.unique(bt[bt >= 0])
         idx = torch.as_tensor(used, dtype=torch.long, device=inp.k_data.device)
         kd = inp.k_data.index_select(0, idx).cpu().numpy()
-        ks = inp.k_scale.index_select(0, idx).cpu().numpy()
+        ks = inp.k_scale.index_select(0, idx).cpu().numpy() if inp.k_scale is not None else None
         remap = np.full(int(bt.max()) + 1 if bt.size else 1, -1, np.int64)
         remap[used] = np.arange(len(used))
         bt = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
     else:
         kd = inp.k_data.cpu().numpy() if inp.k_data.device.type != "cpu" else inp.k_data.numpy()
-        ks = inp.k_scale.cpu().numpy() if inp.k_scale.device.type != "cpu" else inp.k_scale.numpy()
+        ks = None
+        if inp.k_scale is not None:
+            ks = inp.k_scale.cpu().numpy() if inp.k_scale.device.type != "cpu" else inp.k_scale.numpy()
     return oracle.score(mode=mode, q=qn, q_dtype=qdt, k_data=kd, k_scale=ks, page_size=wl.page_size,
+                        k_dtype=wl.k_dtype,
                         block_table=bt, seq_lens=inp.seq_lens.cpu().numpy(),
                         max_seq_len=max_seq_len if max_seq_len is not None else wl.window, sm_scale=sm_scale,
                         cu_seqlens_q=inp.cu_seqlens_q.cpu().numpy(), prefix_lens=inp.prefix_lens.cpu().numpy(),
@@ -97,7 +108,7 @@ class Stats:
 
 
 def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, *, what: str,
-            min_exact: float) -> Stats:
+            min_exact: float, p99_max: Optional[float] = None) -> Stats:
     gpu = np.asarray(gpu, np.float32)
     ref = np.asarray(ref, np.float32)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
@@ -123,6 +134,11 @@ def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, 
     st = Stats(gpu.size, int(fin.sum()), exact, within, max_rel)
     say(f"  {what}: {st.finite}/{st.n} finite, bit-exact {exact:.6f}, within 2^-20 rel {within:.6f}, max rel {max_rel:.3g}")
     assert exact >= min_exact, f"{what}: bit-exact fraction {exact:.6f} below floor {min_exact}"
+    if p99_max is not None and len(r):
+        rel_m = err / np.maximum(sm_scale * m, 1e-300)
+        p99 = float(np.quantile(rel_m, 0.99))
+        say(f"  {what}: err / (sm_scale * M) max {float(rel_m.max()):.3g}, p99 {p99:.3g}")
+        assert p99 <= p99_max, f"{what}: 99th percentile of err / (sm_scale * M) {p99:.3g} above {p99_max:.3g}"
     return st
 
 
@@ -155,10 +171,12 @@ def gpu_inputs(inp: W.Inputs) -> W.Inputs:
         region = inp.region.to(dev)
         out.region = region
         out.k_data = torch.as_strided(region, inp.k_data.shape, inp.k_data.stride(), inp.k_data.storage_offset())
-        out.k_scale = torch.as_strided(region, inp.k_scale.shape, inp.k_scale.stride(), inp.k_scale.storage_offset())
+        if inp.k_scale is not None:
+            out.k_scale = torch.as_strided(region, inp.k_scale.shape, inp.k_scale.stride(),
+                                           inp.k_scale.storage_offset())
     else:
         out.k_data = inp.k_data.to(dev)
-        out.k_scale = inp.k_scale.to(dev)
+        out.k_scale = inp.k_scale.to(dev) if inp.k_scale is not None else None
     return out
 
 

@@ -52,7 +52,8 @@ FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced: every case below 
 
 def valid_args(mode=mx.MXS_MODE_PREFILL):
     q = mx.Query(FAKE, mx.MXS_Q_BF16, 64 * 128, 128, 64)
-    k = mx.KCache(FAKE + 0x100000, 8704, FAKE + 0x100000 + 8192, 8704, 128, 16)
+    k = mx.KCache(data=FAKE + 0x100000, data_page_stride=8704, scale=FAKE + 0x100000 + 8192, scale_page_stride=8704,
+                  page_size=128, k_dtype=mx.MXS_K_MXFP4, num_pages=16)
     b = mx.Batch(FAKE + 0x200000, 16, 16, FAKE + 0x300000, FAKE + 0x300100, FAKE + 0x300200, 1, 64, 64, 1024)
     bs = mx.Out(FAKE + 0x400000, 64 * 8, 8)
     lg = mx.Out(None, 0, 0)
@@ -85,6 +86,10 @@ CASES = [
     ("narrow output rows", lambda q, k, b, bs, lg: setattr(bs, "head_stride", 4), mx.MXS_ELAYOUT),
     ("misaligned output", lambda q, k, b, bs, lg: setattr(bs, "ptr", FAKE + 0x400002), mx.MXS_ELAYOUT),
     ("null query", lambda q, k, b, bs, lg: setattr(q, "ptr", None), mx.MXS_EINVAL),
+    ("unknown cache dtype", lambda q, k, b, bs, lg: setattr(k, "k_dtype", 2), mx.MXS_EDTYPE),
+    ("null scale view (MXFP4)", lambda q, k, b, bs, lg: setattr(k, "scale", None), mx.MXS_EINVAL),
+    # an fp8 cache needs 128 bytes per token: the 8704-byte MXFP4 page stride is too narrow
+    ("narrow fp8 data view", lambda q, k, b, bs, lg: setattr(k, "k_dtype", mx.MXS_K_E4M3), mx.MXS_ELAYOUT),
 ]
 
 
@@ -126,12 +131,37 @@ def test_no_device_is_reported():
     assert call(L, q, k, b, bs, lg) == mx.MXS_EUNSUPPORTED
 
 
+def test_fp8_cache_needs_no_scale_view():
+    # an fp8 cache with 128 B per token and no scale view passes every host
+    # check (without a device the call then stops at the device query)
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a HIP device is visible; this case only runs without one")
+    L = mx.lib()
+    q, k, b, bs, lg = valid_args()
+    k.k_dtype = mx.MXS_K_E4M3
+    k.scale = None
+    k.scale_page_stride = 0
+    k.data_page_stride = 128 * 128
+    assert call(L, q, k, b, bs, lg) == mx.MXS_EUNSUPPORTED
+    k.data_page_stride = 128 * 128 + 8                                   # not a multiple of 16
+    assert call(L, q, k, b, bs, lg) == mx.MXS_ELAYOUT
+
+
 # ------------------------------------------------------------------ planning
 
-def plan_for(L, mode, *, H=64, P=128, B=64, mql=1, msl=131072, lg=0, bs=1, pun=0, cus=256, occ=3, dt=mx.MXS_Q_BF16):
+def plan_for(L, mode, *, H=64, P=128, B=64, mql=1, msl=131072, lg=0, bs=1, pun=0, cus=256, occ=3, dt=mx.MXS_Q_BF16,
+             kd=mx.MXS_K_MXFP4):
     p = mx.Plan()
-    rc = L.mxs_plan_make_for(mode, dt, P, H, B, mql, msl, lg, bs, pun, cus, occ, ctypes.byref(p))
+    rc = L.mxs_plan_make_for(mode, dt, kd, P, H, B, mql, msl, lg, bs, pun, cus, occ, ctypes.byref(p))
     return rc, p
+
+
+def test_plan_records_the_cache_dtype(L):
+    for kd in (mx.MXS_K_MXFP4, mx.MXS_K_E4M3):
+        for mode, kw in [(mx.MXS_MODE_DECODE, {}), (mx.MXS_MODE_PREFILL, dict(B=1, mql=4096))]:
+            rc, p = plan_for(L, mode, kd=kd, **kw)
+            assert rc == 0 and p.k_dtype == kd
 
 
 def test_plan_is_pure(L):
@@ -180,6 +210,7 @@ def test_plan_rejections(L):
     assert plan_for(L, 9)[0] == mx.MXS_EINVAL
     assert plan_for(L, mx.MXS_MODE_DECODE, P=32)[0] == mx.MXS_ELAYOUT
     assert plan_for(L, mx.MXS_MODE_DECODE, dt=5)[0] == mx.MXS_EDTYPE
+    assert plan_for(L, mx.MXS_MODE_DECODE, kd=7)[0] == mx.MXS_EDTYPE
     assert plan_for(L, mx.MXS_MODE_DECODE, H=0)[0] == mx.MXS_EINVAL
     assert plan_for(L, mx.MXS_MODE_LOGITS, lg=0)[0] == mx.MXS_EINVAL
 
@@ -230,6 +261,12 @@ def test_write_pages_rejections_before_device_work(L):
     bad = mx.KCache.from_buffer_copy(bytes(k))
     bad.data_page_stride = 100
     assert w(FAKE, 128, 4, FAKE + 0x1000, bad) == mx.MXS_ELAYOUT
+    bad = mx.KCache.from_buffer_copy(bytes(k))
+    bad.k_dtype = 5
+    assert w(FAKE, 128, 4, FAKE + 0x1000, bad) == mx.MXS_EDTYPE
+    fp8 = mx.KCache.from_buffer_copy(bytes(k))
+    fp8.k_dtype = mx.MXS_K_E4M3                                          # 8704 B < 128 tokens x 128 B
+    assert w(FAKE, 128, 4, FAKE + 0x1000, fp8) == mx.MXS_ELAYOUT
 
 
 def test_python_layer_rejects_cpu_tensors():
@@ -241,3 +278,20 @@ def test_python_layer_rejects_cpu_tensors():
     sl = torch.ones(1, dtype=torch.int32)
     with pytest.raises(ValueError):
         mx.score_decode(q, kd, ks, bt, sl, 128, 0.1)
+
+
+def test_python_layer_fp8_cache_views():
+    import torch
+    # an fp8 cache is a [pages, P, 128] e4m3 (or uint8) view with no scale view
+    k8 = torch.zeros((2, 64, 128), dtype=torch.uint8)
+    kc = mx._kcache(k8, None)
+    assert kc.k_dtype == mx.MXS_K_E4M3 and kc.page_size == 64 and kc.num_pages == 2 and kc.data_page_stride == 8192
+    assert not kc.scale
+    kc = mx._kcache(torch.zeros((3, 128, 64), dtype=torch.uint8), torch.zeros((3, 128, 4), dtype=torch.uint8))
+    assert kc.k_dtype == mx.MXS_K_MXFP4 and kc.num_pages == 3
+    with pytest.raises(ValueError):
+        mx._kcache(torch.zeros((2, 64, 64), dtype=torch.uint8), None)            # MXFP4-shaped data, no scales
+    with pytest.raises(ValueError):
+        mx._kcache(torch.zeros((2, 64, 128), dtype=torch.bfloat16), None)         # not a byte view
+    with pytest.raises(ValueError):
+        mx._kcache(torch.zeros((2, 64, 256), dtype=torch.uint8)[:, :, :128], None)   # token rows not contiguous

@@ -123,3 +123,20 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(writer, "quantize_block", mutant)
     with pytest.raises(AssertionError):
         test_hand_worked_blocks()
+
+
+def test_fp8_cache_writer_hand_worked():
+    # fp8 cache: each element is rounded like the query (nearest e4m3, ties to
+    # even, saturating): 1.0 -> 0x38, 448 -> 0x7E, 500 -> 0x7E (saturated),
+    # -0.0 -> 0x80, 1.0625 -> 0x38 (tie to even), 1.1875 -> 0x3A (tie to even);
+    # element e at byte e of the token's 128-byte row.
+    bits = np.zeros((2, 128), dtype=np.uint16)
+    vals = [1.0, 448.0, 500.0, -0.0, 1.0625, 1.1875]
+    for e, v in enumerate(vals):
+        bits[1, 10 + e] = bf16_bits(v)
+    kd = np.zeros((2, 64, 128), dtype=np.uint8)
+    writer.write_pages_e4m3(bits, [-1, 64 + 3], kd, 64)                  # token 0 skipped; token 1 -> page 1, slot 3
+    row = kd[1, 3]
+    assert list(row[10:16]) == [0x38, 0x7E, 0x7E, 0x80, 0x38, 0x3A]
+    assert int(row.sum()) == sum([0x38, 0x7E, 0x7E, 0x80, 0x38, 0x3A])
+    assert kd[0].sum() == 0 and kd[1, :3].sum() == 0 and kd[1, 4:].sum() == 0
