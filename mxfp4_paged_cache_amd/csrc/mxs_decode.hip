@@ -10,10 +10,9 @@ using namespace dev;
 // Each page is read by exactly one wave, so K goes straight from HBM into
 // registers (staging it in LDS would buy nothing): per 16-token tile, lane
 // (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
-// per wave instruction) and e8m0 byte g of that token; from an fp8 cache,
-// bytes 16g..16g+15 and 64+16g..64+16g+15 of the token (2 KB per tile). Pages are double-
-// buffered in registers: the loads of page j+2 are in flight while page j+1
-// is scored. The chunk's page ids are read once into one VGPR (lane l holds
+// per wave instruction) and e8m0 byte g of that token (an fp8 page takes a
+// detour through LDS, see below). Pages are double-buffered in registers:
+// the loads of page j+2 are in flight while page j+1 is scored. The chunk's page ids are read once into one VGPR (lane l holds
 // the id of page j0 + l) and picked per page with readlane.
 //
 // Wave items are ordered page chunk fastest, and the plan makes the chunk
@@ -25,8 +24,8 @@ using namespace dev;
 // request's query and block-table row to every chunk.
 // ---------------------------------------------------------------------------
 // One page in registers. load(): dp/sp are the page's (uniform) bases,
-// doff/soff the lane's byte offsets inside the page (MXFP4 data 64 i + 16 g,
-// scale 4 i + g; fp8 data 128 i + 16 g, whose second slice is 64 bytes on).
+// doff/soff the lane's byte offsets inside the page (MXFP4: data 64 i + 16 g,
+// scale 4 i + g; fp8: 16 * lane).
 template <int KDT, int P>
 struct RegPage;
 
@@ -45,43 +44,55 @@ struct RegPage<MXS_K_MXFP4, P> {
   }
 };
 
+// fp8: a 16-token tile is 2 KB. Loaded as two contiguous 1 KB blocks (chunk
+// `lane` and chunk 64 + `lane` of the tile), which the MFMA cannot take
+// directly (its row i must sit in lanes i, i + 16, ...); each half page goes
+// through the wave's LDS buffer in the fp8 tile layout and is read back per
+// tile. Loading each token's slices straight into their MFMA lanes instead
+// (16 pieces of 64 bytes per instruction) measured about 20% slower.
 template <int P>
 struct RegPage<MXS_K_E4M3, P> {
-  u4 lo[P / 16];
-  u4 hi[P / 16];
-  static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(i * 128 + 16 * g); }
-  __device__ __forceinline__ KTile<MXS_K_E4M3> tile(int t) const { return {lo[t], hi[t]}; }
+  u4 c0[P / 16];   // chunk `lane` of tile t
+  u4 c1[P / 16];   // chunk 64 + `lane` of tile t
+  static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(16 * (16 * g + i)); }
   __device__ __forceinline__ void load(const uint8_t* dp, const uint8_t*, uint32_t doff, uint32_t) {
 #pragma unroll
     for (int t = 0; t < P / 16; ++t) {
-      lo[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t));
-      hi[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t + 64u));
+      c0[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t));
+      c1[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t + 1024u));
+    }
+  }
+  // tiles [HF * P / 32, (HF + 1) * P / 32) into buf (P * 64 bytes) as tiles 0.. of the fp8 layout
+  template <int HF>
+  __device__ __forceinline__ void stage_half(uint8_t* buf, int lane) const {
+#pragma unroll
+    for (int u = 0; u < P / 32; ++u) {
+      *reinterpret_cast<u4*>(buf + fp8_chunk_slot(u, lane)) = c0[HF * (P / 32) + u];
+      *reinterpret_cast<u4*>(buf + fp8_chunk_slot(u, 64 + lane)) = c1[HF * (P / 32) + u];
     }
   }
 };
 
-// Score one register-resident page against the wave's four query tiles.
-// MASK: the page holds the end of the live window (tokens >= lip are dead).
-// The tile loop is software-pipelined by hand: the four MFMAs of tile t are
-// issued before the results of tile t-1 are folded, and a scheduling fence
-// after each step keeps only two tiles of results live.
-template <int KDT, int P, bool MASK, bool LG>
-__device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i (&qt)[4], int j, int lip, int g,
-                                            const bool (&hv)[4], float* stage, int jrel, float* lg_row,
-                                            const int64_t (&hoff)[4], const KArgs& a) {
-  constexpr int TPP = P / 16;
+// MFMAs and folds of tiles [T0, T1) of one page against the wave's four query
+// tiles; tile(t) gives the K operand of tile t. MASK: the page holds the end
+// of the live window (token 16 t + 4 g + v is live iff 16 t + v < lrel). The
+// loop is software-pipelined by hand: the four MFMAs of tile t are issued
+// before the results of tile t-1 are folded, and a scheduling fence after
+// each step keeps only two tiles of results live.
+template <int P, bool MASK, bool LG, int T0, int T1, typename Tile>
+__device__ __forceinline__ void decode_tiles(const Tile& tile, const v8i (&qt)[4], int j, int lrel, int g,
+                                             const bool (&hv)[4], float* lg_row, const int64_t (&hoff)[4],
+                                             const KArgs& a, float (&m)[4]) {
   const float s = a.sm_scale;
-  float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
   v4f prev[4];
-  const int lrel = lip - 4 * g;   // token 16 tp + 4 g + v is live iff 16 tp + v < lrel
 #pragma unroll
-  for (int t = 0; t <= TPP; ++t) {
+  for (int t = T0; t <= T1; ++t) {
     v4f cur[4];
-    if (t < TPP) {
+    if (t < T1) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) cur[n] = mma_tile(kp.tile(t), qt[n]);
+      for (int n = 0; n < 4; ++n) cur[n] = mma_tile(tile(t), qt[n]);
     }
-    if (t > 0) {
+    if (t > T0) {
       const int tp = t - 1;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -98,12 +109,39 @@ __device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i
         }
       }
     }
-    if (t < TPP) {
+    if (t < T1) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) prev[n] = cur[n];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Score one register-resident page (MASK: tokens >= lip are dead) and stage
+// its block scores; kbuf is the wave's LDS buffer (fp8 only).
+template <int KDT, int P, bool MASK, bool LG>
+__device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i (&qt)[4], int j, int lip, int g,
+                                            const bool (&hv)[4], float* stage, int jrel, float* lg_row,
+                                            const int64_t (&hoff)[4], const KArgs& a, uint8_t* kbuf) {
+  constexpr int TPP = P / 16;
+  float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  const int lrel = lip - 4 * g;
+  if constexpr (KDT == MXS_K_MXFP4) {
+    decode_tiles<P, MASK, LG, 0, TPP>([&](int t) { return kp.tile(t); }, qt, j, lrel, g, hv, lg_row, hoff, a, m);
+  } else {
+    constexpr int HT = TPP / 2;
+    const int lane = threadIdx.x & 63, i = lane & 15;
+    auto from_lds = [&](int t0) { return [=](int t) { return lds_tile<MXS_K_E4M3, P>(kbuf, g, i, t - t0); }; };
+    wave_lds_sync();   // the previous page's reads of kbuf are done
+    kp.template stage_half<0>(kbuf, lane);
+    wave_lds_sync();
+    decode_tiles<P, MASK, LG, 0, HT>(from_lds(0), qt, j, lrel, g, hv, lg_row, hoff, a, m);
+    wave_lds_sync();
+    kp.template stage_half<1>(kbuf, lane);
+    wave_lds_sync();
+    decode_tiles<P, MASK, LG, HT, TPP>(from_lds(HT), qt, j, lrel, g, hv, lg_row, hoff, a, m);
+  }
+  const float s = a.sm_scale;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const float r = fold_groups(m[n]);
@@ -163,6 +201,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   // this wave's staging area for its block scores: [64 heads][pages of the chunk]
   __shared__ float stage_all[kWaves][kDecodeHeads * kDecodeStageStride];
   float* stage = stage_all[wave];
+  // fp8: this wave's half-page K buffer (P * 64 bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf_all[kWaves][KDT == MXS_K_E4M3 ? P * 64 : 16];
+  uint8_t* kbuf = kbuf_all[wave];
 
   if (j0 < jl) {
     const uint32_t doff = RegPage<KDT, P>::data_offset(g, i);
@@ -176,9 +217,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
     auto score = [&](const RegPage<KDT, P>& kp, int j) {
       const int lip = limit - j * P;                 // live tokens in this page
       if (lip >= P)
-        decode_page<KDT, P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+        decode_page<KDT, P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a, kbuf);
       else
-        decode_page<KDT, P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a);
+        decode_page<KDT, P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a, kbuf);
     };
     RegPage<KDT, P> A, B;
     load_page(A, j0);

@@ -178,19 +178,37 @@ constexpr int kStagedPageBytes = KDT == MXS_K_E4M3 ? P * 128 : P * 68;
 // as [lane group g][row i][16 bytes] at 1024 t + 256 g + 16 i, so the 16
 // lanes of a group read 256 contiguous bytes (no bank conflicts on
 // ds_read_b128); the scales follow as [token][4 bytes] at P * 64. fp8: tile t
-// is [half h][g][i][16 bytes] at 2048 t + 1024 h + 256 g + 16 i, half h
-// holding bytes 64 h + 16 g .. + 15 of token 16 t + i.
+// is [half h][g][row][16 bytes] at 2048 t + 1024 h + 256 g + 16 (i ^ (4 h + g)),
+// half h holding bytes 64 h + 16 g .. + 15 of token 16 t + i. The XOR keeps
+// the 16 lanes of a group on 16 distinct 16-byte slots of one 256-byte run
+// when reading, and sends the 8 chunks of one token (written by 8 adjacent
+// lanes) to 8 distinct banks when staging.
 template <int KDT, int P>
 __device__ __forceinline__ KTile<KDT> lds_tile(const uint8_t* kb, int g, int i, int t) {
   KTile<KDT> r;
   if constexpr (KDT == MXS_K_E4M3) {
-    r.lo = *reinterpret_cast<const u4*>(kb + 2048 * t + 256 * g + 16 * i);
-    r.hi = *reinterpret_cast<const u4*>(kb + 2048 * t + 1024 + 256 * g + 16 * i);
+    r.lo = *reinterpret_cast<const u4*>(kb + 2048 * t + 256 * g + 16 * (i ^ g));
+    r.hi = *reinterpret_cast<const u4*>(kb + 2048 * t + 1024 + 256 * g + 16 * (i ^ (4 + g)));
   } else {
     r.d = *reinterpret_cast<const u4*>(kb + 1024 * t + 256 * g + 16 * i);
     r.s = kb[P * 64 + 64 * t + 4 * i + g];
   }
   return r;
+}
+
+// Byte offset of 16-byte chunk c (0..127: token c / 8 of the tile, chunk c % 8
+// of its 128 bytes) of fp8 tile `tile` in the layout above.
+__device__ __forceinline__ int fp8_chunk_slot(int tile, int c) {
+  return tile * 2048 + ((c & 7) >> 2) * 1024 + (c & 3) * 256 + (((c >> 3) & 15) ^ (c & 7)) * 16;
+}
+
+// Order a wave's own LDS writes before its later LDS reads of other lanes'
+// data (and reads before later writes): a wave's LDS operations complete in
+// program order; the fences keep the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // One page of K staged through registers into LDS by a whole workgroup.
@@ -230,9 +248,7 @@ __device__ __forceinline__ void stage_store(const PageStage<KDT, P>& st, uint8_t
   for (int c = 0; c < PageStage<KDT, P>::kDataChunks; ++c) {
     const int sl = tid + kThreads * c;
     if constexpr (KDT == MXS_K_E4M3) {
-      const int tok = sl >> 3, c8 = sl & 7;
-      const int at = (tok >> 4) * 2048 + (c8 >> 2) * 1024 + (c8 & 3) * 256 + (tok & 15) * 16;
-      *reinterpret_cast<u4*>(buf + at) = st.d[c];
+      *reinterpret_cast<u4*>(buf + fp8_chunk_slot(sl >> 7, sl & 127)) = st.d[c];
     } else {
       *reinterpret_cast<u4*>(buf + 16 * sl) = st.d[c];
     }
