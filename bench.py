@@ -66,9 +66,9 @@ def kernel_name(wl) -> str:
         return "k_select"
     if wl.write_tokens:
         return "k_write"
-    if wl.mode == "decode":
-        return "k_decode"
-    return "k_logits" if (wl.mode == "logits" or wl.want_logits) else "k_prefill"
+    if wl.mode == "logits" or wl.want_logits:
+        return "k_logits"
+    return "k_decode" if wl.mode == "decode" else "k_prefill"
 
 
 def kernel_source_hash(kernel: str) -> str:

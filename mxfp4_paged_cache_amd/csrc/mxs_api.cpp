@@ -380,7 +380,7 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t pa
   const int64_t NB = ceil_div(max_seq_len, page_size);
   const int64_t capacity = (int64_t)num_cus * wg_per_cu;   // resident workgroups
 
-  if (mode == MXS_MODE_DECODE) {
+  if (mode == MXS_MODE_DECODE && !want_logits) {
     // One wave per (request, 64-head group, page chunk). Chunks are sized so
     // that the waves fill the resident capacity about once (aiter #5518,
     // decode auto-CTA: host-known buckets), or the requested unit count.
@@ -402,8 +402,9 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t pa
     p.grid = (int32_t)ceil_div(p.items, mxs::kWaves);
   } else {
     // Work item = (request, block of query slots, chunk of pages); the grid
-    // loops over the items. Logits (asked for by either call) come from the
-    // logits kernel, block scores alone from the block-score kernel.
+    // loops over the items. Logits (asked for by any call, decode included:
+    // a decode request is one row with one query) come from the logits
+    // kernel, prefill block scores alone from the block-score kernel.
     const bool lgk = mode == MXS_MODE_LOGITS || want_logits;
     p.kernel = lgk ? mxs::KID_LOGITS : mxs::KID_PREFILL;
     p.head_groups = 1;
@@ -473,8 +474,8 @@ int mxs_plan_make(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t page_s
     return fail(MXS_EDTYPE, "query dtype must be bf16 or e4m3; got %d", q_dtype);
   if (check_k_dtype(k_dtype)) return MXS_EDTYPE;
   if (page_size != 64 && page_size != 128) return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", page_size);
-  const int32_t kid = mode == MXS_MODE_DECODE                    ? mxs::KID_DECODE
-                      : (mode == MXS_MODE_LOGITS || want_logits) ? mxs::KID_LOGITS
+  const int32_t kid = (mode == MXS_MODE_LOGITS || want_logits) ? mxs::KID_LOGITS
+                      : mode == MXS_MODE_DECODE                  ? mxs::KID_DECODE
                                                                  : mxs::KID_PREFILL;
   const int occ = occupancy_cached(dev, kid, q_dtype, k_dtype, page_size, want_blocks != 0, want_logits != 0);
   return mxs_plan_make_for(mode, q_dtype, k_dtype, page_size, num_heads, batch, max_query_len, max_seq_len,
@@ -508,7 +509,7 @@ int check_out(const char* name, const mxs_out* o, int64_t rows, int32_t H, int64
 bool plan_consistent(const mxs_plan& p, int mode, int32_t H, int32_t B, int32_t max_query_len, int64_t NB) {
   if (p.block != mxs::kThreads || p.grid < 1 || p.pages_per_item < 1 || p.page_items < 1) return false;
   if ((int64_t)p.page_items * p.pages_per_item < NB) return false;
-  if (mode == MXS_MODE_DECODE) {
+  if (mode == MXS_MODE_DECODE && !p.want_logits) {
     return p.kernel == mxs::KID_DECODE && p.head_groups == ceil_div(H, mxs::kDecodeHeads) &&
            p.pages_per_item <= mxs::kDecodeMaxPages && p.page_items % mxs::kWaves == 0 &&
            p.items == (int64_t)B * p.head_groups * p.page_items && (int64_t)p.grid * mxs::kWaves == p.items;
@@ -645,6 +646,7 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   a.page_items = plan.page_items;
   a.head_groups = plan.head_groups;
   a.items = plan.items;
+  a.decode_rows = decode && plan.kernel == mxs::KID_LOGITS ? 1 : 0;
   hipError_t e = mxs::launch(plan, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MXS_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   return MXS_OK;

@@ -6,7 +6,10 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
-// Decode: one wave per (request, group of 64 heads, chunk of <= 32 pages).
+// Decode block scores: one wave per (request, group of 64 heads, chunk of <=
+// 32 pages). (Decode calls that also want logits run on the logits kernel,
+// one query row per request: its LDS windows write logit rows far faster
+// than this kernel's MFMA layout would.)
 // Each page is read by exactly one wave, so K goes straight from HBM into
 // registers (staging it in LDS would buy nothing): per 16-token tile, lane
 // (g, i) loads bytes 16g..16g+15 of token 16t+i (one 1 KB contiguous block
@@ -79,11 +82,8 @@ struct RegPage<MXS_K_E4M3, P> {
 // loop is software-pipelined by hand: the four MFMAs of tile t are issued
 // before the results of tile t-1 are folded, and a scheduling fence after
 // each step keeps only two tiles of results live.
-template <int P, bool MASK, bool LG, int T0, int T1, typename Tile>
-__device__ __forceinline__ void decode_tiles(const Tile& tile, const v8i (&qt)[4], int j, int lrel, int g,
-                                             const bool (&hv)[4], float* lg_row, const int64_t (&hoff)[4],
-                                             const KArgs& a, float (&m)[4]) {
-  const float s = a.sm_scale;
+template <int MASK, int T0, int T1, typename Tile>
+__device__ __forceinline__ void decode_tiles(const Tile& tile, const v8i (&qt)[4], int lrel, float (&m)[4]) {
   v4f prev[4];
 #pragma unroll
   for (int t = T0; t <= T1; ++t) {
@@ -102,11 +102,6 @@ __device__ __forceinline__ void decode_tiles(const Tile& tile, const v8i (&qt)[4
           for (int v = 0; v < 4; ++v) c[v] = (16 * tp + v < lrel) ? c[v] : kNegInf;
         }
         m[n] = max_into(m[n], c);
-        if constexpr (LG) {
-          if (hv[n])
-            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * tp + 4 * g, c * s, a.max_seq_len,
-                          a.vec_lg);
-        }
       }
     }
     if (t < T1) {
@@ -119,15 +114,14 @@ __device__ __forceinline__ void decode_tiles(const Tile& tile, const v8i (&qt)[4
 
 // Score one register-resident page (MASK: tokens >= lip are dead) and stage
 // its block scores; kbuf is the wave's LDS buffer (fp8 only).
-template <int KDT, int P, bool MASK, bool LG>
-__device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i (&qt)[4], int j, int lip, int g,
-                                            const bool (&hv)[4], float* stage, int jrel, float* lg_row,
-                                            const int64_t (&hoff)[4], const KArgs& a, uint8_t* kbuf) {
+template <int KDT, int P, bool MASK>
+__device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i (&qt)[4], int lip, int g,
+                                            float* stage, int jrel, const KArgs& a, uint8_t* kbuf) {
   constexpr int TPP = P / 16;
   float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
   const int lrel = lip - 4 * g;
   if constexpr (KDT == MXS_K_MXFP4) {
-    decode_tiles<P, MASK, LG, 0, TPP>([&](int t) { return kp.tile(t); }, qt, j, lrel, g, hv, lg_row, hoff, a, m);
+    decode_tiles<MASK, 0, TPP>([&](int t) { return kp.tile(t); }, qt, lrel, m);
   } else {
     constexpr int HT = TPP / 2;
     const int lane = threadIdx.x & 63, i = lane & 15;
@@ -135,11 +129,11 @@ __device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i
     wave_lds_sync();   // the previous page's reads of kbuf are done
     kp.template stage_half<0>(kbuf, lane);
     wave_lds_sync();
-    decode_tiles<P, MASK, LG, 0, HT>(from_lds(0), qt, j, lrel, g, hv, lg_row, hoff, a, m);
+    decode_tiles<MASK, 0, HT>(from_lds(0), qt, lrel, m);
     wave_lds_sync();
     kp.template stage_half<1>(kbuf, lane);
     wave_lds_sync();
-    decode_tiles<P, MASK, LG, HT, TPP>(from_lds(HT), qt, j, lrel, g, hv, lg_row, hoff, a, m);
+    decode_tiles<MASK, HT, TPP>(from_lds(HT), qt, lrel, m);
   }
   const float s = a.sm_scale;
 #pragma unroll
@@ -149,9 +143,8 @@ __device__ __forceinline__ void decode_page(const RegPage<KDT, P>& kp, const v8i
   }
 }
 
-template <int QDT, int KDT, int P, bool LG>
+template <int QDT, int KDT, int P>
 __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
-  constexpr int TPP = P / 16;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, i = lane & 15;
   // the wave index is uniform across the wave: keep everything derived from it scalar
@@ -187,17 +180,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   __syncthreads();
   if (!active) return;
   v8i qt[4];
-  bool hv[4];
-  int64_t hoff[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int h = hg * kDecodeHeads + n * 16 + i;
-    hv[n] = h < a.H;
-    hoff[n] = (int64_t)(hv[n] ? h : a.H - 1);
-    qt[n] = q_share[n][lane];
-  }
+  for (int n = 0; n < 4; ++n) qt[n] = q_share[n][lane];
   float* bs_row = a.bs + (int64_t)b * a.bs_row_stride;
-  float* lg_row = LG ? a.lg + (int64_t)b * a.lg_row_stride : nullptr;
   // this wave's staging area for its block scores: [64 heads][pages of the chunk]
   __shared__ float stage_all[kWaves][kDecodeHeads * kDecodeStageStride];
   float* stage = stage_all[wave];
@@ -217,9 +202,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
     auto score = [&](const RegPage<KDT, P>& kp, int j) {
       const int lip = limit - j * P;                 // live tokens in this page
       if (lip >= P)
-        decode_page<KDT, P, false, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a, kbuf);
+        decode_page<KDT, P, false>(kp, qt, lip, g, stage, j - j0, a, kbuf);
       else
-        decode_page<KDT, P, true, LG>(kp, qt, j, lip, g, hv, stage, j - j0, lg_row, hoff, a, kbuf);
+        decode_page<KDT, P, true>(kp, qt, lip, g, stage, j - j0, a, kbuf);
     };
     RegPage<KDT, P> A, B;
     load_page(A, j0);
@@ -242,17 +227,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
     if (g == 0)
 #pragma unroll
       for (int n = 0; n < 4; ++n) stage[(16 * n + i) * kDecodeStageStride + (j - j0)] = kNegInf;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (hv[n]) {
-        if constexpr (LG) {
-          const v4f ninf = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-          for (int t = 0; t < TPP; ++t)
-            store_logits4(lg_row + hoff[n] * a.lg_head_stride, j * P + 16 * t + 4 * g, ninf, a.max_seq_len, a.vec_lg);
-        }
-      }
-    }
   }
   // Block scores leave LDS as one contiguous run of (j1 - j0) floats per head:
   // consecutive lanes write consecutive pages, so every store instruction
@@ -277,15 +251,14 @@ template <int QDT, int KDT, int P>
 struct Launch {
   static hipError_t run(const mxs_plan& plan, const KArgs& a, hipStream_t stream) {
     void* args[] = {const_cast<KArgs*>(&a)};
-    const void* fn = a.lg ? reinterpret_cast<const void*>(&k_decode<QDT, KDT, P, true>)
-                          : reinterpret_cast<const void*>(&k_decode<QDT, KDT, P, false>);
-    return hipLaunchKernel(fn, dim3(plan.grid), dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_decode<QDT, KDT, P>), dim3(plan.grid), dim3(kThreads),
+                           args, 0, stream);
   }
 };
 
 template <int QDT, int KDT, int P>
 struct Occupancy {
-  static int run(bool lg) { return lg ? occ_of(&k_decode<QDT, KDT, P, true>) : occ_of(&k_decode<QDT, KDT, P, false>); }
+  static int run() { return occ_of(&k_decode<QDT, KDT, P>); }
 };
 
 }  // namespace
@@ -294,8 +267,8 @@ hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t strea
   return dispatch_variant<Launch>(plan.q_dtype, plan.k_dtype, plan.page_size, plan, a, stream);
 }
 
-int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_lg) {
-  return dispatch_variant<Occupancy>(q_dtype, k_dtype, page_size, want_lg);
+int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size) {
+  return dispatch_variant<Occupancy>(q_dtype, k_dtype, page_size);
 }
 
 }  // namespace mxs

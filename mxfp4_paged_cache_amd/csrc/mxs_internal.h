@@ -12,9 +12,10 @@ namespace mxs {
 
 // Kernel ids stored in mxs_plan::kernel.
 enum KernelId : int32_t {
-  KID_DECODE = 1,     // one wave per (request, head group, page chunk); K straight to registers
+  KID_DECODE = 1,     // decode block scores: one wave per (request, head group, page chunk)
   KID_PREFILL = 2,    // block scores: workgroup per (request, 512 slots, page chunk); K staged in LDS
-  KID_LOGITS = 3,     // logits (+ block scores): workgroup per (request, 64 slots, page chunk); output via LDS windows
+  KID_LOGITS = 3,     // logits (+ block scores), prefill or decode rows: workgroup per (request, 64 slots,
+                      // page chunk); output via LDS windows
 };
 
 constexpr int kWaves = 4;           // waves per workgroup, every kernel
@@ -63,6 +64,7 @@ struct KArgs {
   int64_t items;
   int32_t vec_bs;           // widest vector store the block-score rows allow, in floats (4, 2 or 1)
   int32_t vec_lg;           // logit rows 16-byte aligned
+  int32_t decode_rows;      // logits kernel: row b is request b (one query row, limit = seq_len[b])
 };
 
 // Arguments of the page-selection kernel (mxs_select.hip).
@@ -110,7 +112,7 @@ hipError_t launch_prefill(const mxs_plan& plan, const KArgs& a, hipStream_t stre
 hipError_t launch_logits(const mxs_plan& plan, const KArgs& a, hipStream_t stream);
 
 // Workgroups of the kernel variant (q dtype, cache dtype, page size, outputs) that fit on one CU.
-int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_lg);
+int occupancy_decode(int32_t q_dtype, int32_t k_dtype, int32_t page_size);
 int occupancy_prefill(int32_t q_dtype, int32_t k_dtype, int32_t page_size);
 int occupancy_logits(int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs);
 
@@ -121,7 +123,7 @@ inline hipError_t launch(const mxs_plan& plan, const KArgs& a, hipStream_t strea
 }
 
 inline int occupancy(int32_t kernel, int32_t q_dtype, int32_t k_dtype, int32_t page_size, bool want_bs, bool want_lg) {
-  return kernel == KID_DECODE    ? occupancy_decode(q_dtype, k_dtype, page_size, want_lg)
+  return kernel == KID_DECODE    ? occupancy_decode(q_dtype, k_dtype, page_size)
          : kernel == KID_PREFILL ? occupancy_prefill(q_dtype, k_dtype, page_size)
                                  : occupancy_logits(q_dtype, k_dtype, page_size, want_bs);
 }

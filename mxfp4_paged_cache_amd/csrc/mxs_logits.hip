@@ -52,12 +52,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     const int64_t rest = item / a.page_items;
     const int sb = (int)(rest % a.slot_items);
     const int b = (int)(rest / a.slot_items);
-    const int row0 = a.cu[b];
-    const int qlen = a.cu[b + 1] - row0;
+    // decode rows: request b is row b with one query, seeing its seq_len tokens
+    const int row0 = a.decode_rows ? b : a.cu[b];
+    const int qlen = a.decode_rows ? 1 : a.cu[b + 1] - row0;
     const int64_t nslots = (int64_t)qlen * a.H;
     const int64_t sbeg = (int64_t)sb * kLogitsSlots;
     if (sbeg >= nslots) continue;   // uniform over the workgroup
-    const int seq = a.seq[b], pre = a.prefix[b];
+    const int seq = a.seq[b], pre = a.decode_rows ? seq - 1 : a.prefix[b];
     const int64_t slast = min(sbeg + (int64_t)kLogitsSlots, nslots) - 1;
     const int item_lim = clampi(min(seq, pre + (int)(slast / a.H) + 1), 0, W);
 

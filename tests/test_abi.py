@@ -189,6 +189,20 @@ def test_decode_plan_covers_every_page_once(L):
         assert p.grid * 4 == p.items
 
 
+def test_decode_with_logits_plans_the_logits_kernel(L):
+    # a decode request is one query row: with logits it runs on the logits
+    # kernel (64 query slots per item), block scores alone on the decode kernel
+    for B, H, msl in [(64, 64, 131072), (5, 64, 1030), (3, 4, 256)]:
+        rc, p = plan_for(L, mx.MXS_MODE_DECODE, B=B, H=H, msl=msl, lg=1)
+        assert rc == 0
+        assert p.kernel == 3 and p.max_query_len == 1
+        assert p.slot_items * p.slots_per_item >= H
+        assert p.page_items * p.pages_per_item >= (msl + 127) // 128
+        assert p.items == B * p.slot_items * p.page_items
+        rc, p0 = plan_for(L, mx.MXS_MODE_DECODE, B=B, H=H, msl=msl, lg=0)
+        assert rc == 0 and p0.kernel == 1
+
+
 def test_prefill_plan_covers_every_slot(L):
     for B, mql, H, msl in [(1, 4096, 64, 131072), (1, 32768, 64, 132768), (3, 17, 2, 300), (8, 128, 64, 8192)]:
         rc, p = plan_for(L, mx.MXS_MODE_PREFILL, B=B, mql=mql, H=H, msl=msl)
