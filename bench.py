@@ -30,7 +30,8 @@ the roofline picks up while the kernel sources still hash the same.
 5: logits, 64-token pages in a shared pool past 4.608e9 bytes, 6: top-64 page
 selection over the block scores of config 3, 7: writing 2^20 bf16 keys into
 MXFP4 page slots; 8, 9, 10: configs 2, 3 and 7 over an fp8 (e4m3, 128 B per
-token) index cache, the format the MXFP4 one replaces).
+token) index cache, the format the MXFP4 one replaces; 11: paged MXFP4
+attention decode, 2048 rows x 16 query heads over 2048 tokens of K and V).
 """
 from __future__ import annotations
 
@@ -66,6 +67,8 @@ def kernel_name(wl) -> str:
         return "k_select"
     if wl.write_tokens:
         return "k_write"
+    if wl.attn_group:
+        return "k_attn"
     if wl.mode == "logits" or wl.want_logits:
         return "k_logits"
     return "k_decode" if wl.mode == "decode" else "k_prefill"
@@ -127,6 +130,8 @@ def pmc_summary(dbs):
 
 def path_dtype(wl) -> str:
     """The arithmetic type the measured path computes in."""
+    if wl.attn_group:
+        return "e2m1 x e4m3 -> f32; bf16 x bf16 -> f32; bf16 out"
     if wl.write_tokens:
         return "bf16 -> e4m3" if wl.k_dtype == "e4m3" else "bf16 -> e2m1 + e8m0"
     if wl.select_k:
@@ -146,6 +151,13 @@ def algorithmic_bytes(wl, inp) -> int:
         # the selection reads every block score and writes k page ids per (row, head)
         return wl.T * wl.H * (wl.NB + wl.select_k) * 4 + (wl.B * 3 + 1) * 4
     P = wl.page_size
+    if wl.attn_group:
+        # K and V of every live page (68 B per token each, per kv head), the query, the bf16
+        # output, the live table entries and the context lengths
+        pages = sum((min(s, wl.window) + P - 1) // P for s in wl.seq_lens)
+        hq = wl.H * wl.attn_group
+        qb = 2 if wl.q_dtype == "bf16" else 1
+        return pages * P * 136 * wl.H + wl.T * hq * 128 * (qb + 2) + pages * 4 + wl.B * 4
     pages = sum((min(s, wl.window) + P - 1) // P for s in wl.seq_lens)
     kbytes = pages * P * token_bytes
     qbytes = wl.T * wl.H * 128 * (2 if wl.q_dtype == "bf16" else 1)
@@ -217,11 +229,14 @@ def main():
     NB, Wd = wl.NB, wl.window
     S = W.INV_SQRT_D
 
-    bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if wl.want_blocks else None
+    bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if (wl.want_blocks and not wl.attn_group) else None
     lg = torch.empty((T, H, Wd), dtype=torch.float32, device=dev) if wl.want_logits else None
-    plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks,
-                        k_dtype=wl.k_dtype)
-    log(f"plan: {plan.as_dict()}")
+    plan = None
+    if not wl.attn_group:
+        plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks,
+                            k_dtype=wl.k_dtype)
+        log(f"plan: {plan.as_dict()}")
+    ao = torch.empty((T, H * wl.attn_group, 128), dtype=torch.bfloat16, device=dev) if wl.attn_group else None
 
     sel = None
     if wl.select_k:
@@ -242,7 +257,10 @@ def main():
 
     def call(i):
         bt = inp.block_tables[i % len(inp.block_tables)]
-        if wl.write_tokens:
+        if wl.attn_group:
+            mx.attn_decode(inp.q, inp.k_data, inp.k_scale, inp.extras["v_data"], inp.extras["v_scale"], bt,
+                           inp.seq_lens, Wd, S, out=ao)
+        elif wl.write_tokens:
             mx.write_pages(wk, wslots, inp.k_data, inp.k_scale)
         elif wl.select_k:
             mx.select_pages(bs, wl.select_k, inp.seq_lens, Wd, P, cu_seqlens_q=inp.cu_seqlens_q,
@@ -299,12 +317,13 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms = ms_total / args.steps   # one kernel launch per step: this is the launch's average duration
 
-    triples = wl.live_triples()
+    # live (row, query head, token) triples; attention counts every query head of every kv head
+    triples = wl.live_triples() * (wl.attn_group or 1)
     # throughput: scored (row, head, token) triples/s; the selection consumes (row, head, page) block scores
     units = wl.write_tokens if wl.write_tokens else (wl.T * wl.H * wl.NB if wl.select_k else triples)
     value = units / (ms / 1e3)
     abytes = algorithmic_bytes(wl, inp)
-    flops = 2.0 * 128 * triples
+    flops = (4.0 if wl.attn_group else 2.0) * 128 * triples   # attention: Q.K and P.V
     gbps = abytes / (ms / 1e3) / 1e9
     tflops = flops / (ms / 1e3) / 1e12
     hbm_bound = (wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k) or
@@ -326,7 +345,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        if wl.write_tokens:
+        if wl.attn_group:
+            cpu = cpu_baseline_attn(wl, inp, args.cpu_sample)
+        elif wl.write_tokens:
             cpu = cpu_baseline_write(wl, wk, wslots, args.cpu_sample)
         elif wl.select_k:
             cpu = cpu_baseline_select(wl, bs, inp, args.cpu_sample)
@@ -350,13 +371,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "query_rows": T, "heads": H, "head_dim": 128,
                    "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype, "cache": wl.k_dtype,
-                   "e8m0_range": [wl.scale_lo, wl.scale_hi], "outputs": ("block_scores" if wl.want_blocks else "") +
-                   ("+logits" if wl.want_logits else ""), "rotating_tables": len(inp.block_tables),
+                   "e8m0_range": [wl.scale_lo, wl.scale_hi],
+                   "outputs": "attention" if wl.attn_group else (("block_scores" if wl.want_blocks else "") +
+                                                                  ("+logits" if wl.want_logits else "")), "rotating_tables": len(inp.block_tables),
                    **({"select_k": wl.select_k} if wl.select_k else {}),
-                   **({"write_tokens": wl.write_tokens} if wl.write_tokens else {})},
+                   **({"write_tokens": wl.write_tokens} if wl.write_tokens else {}),
+                   **({"query_heads_per_kv_head": wl.attn_group} if wl.attn_group else {})},
         "hbm_gbps": round(gbps, 1),
         "mfma_tflops": None if (wl.select_k or wl.write_tokens) else round(tflops, 2),
-        "mfma_util_fp8_rate": None if (wl.select_k or wl.write_tokens) else round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+        "mfma_util_fp8_rate": None if (wl.select_k or wl.write_tokens or wl.attn_group) else round(
+            tflops / MFMA_FP8_PEAK_TFLOPS, 4),
         "algorithmic_bytes": abytes,
         "live_triples": None if (wl.select_k or wl.write_tokens) else triples,
         "roofline": roof,
@@ -389,6 +413,34 @@ def cpu_baseline_write(wl, wk, wslots, sample_tokens: int):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} of {wl.write_tokens} keys, {dt:.2f} s"}
+
+
+def cpu_baseline_attn(wl, inp, sample_rows: int):
+    """The attention oracle (test infrastructure, numpy float64) on a bounded
+    sample of rows; reported as (row, query head, token) triples/s."""
+    import numpy as np
+    import torch
+    from oracle import attn
+    n = sample_rows or wl.T   # ~0.13 s per 32 rows of 2048 tokens x 16 heads: every row is ~8 s
+    rows = np.sort(np.random.default_rng(1234).choice(wl.T, size=min(n, wl.T), replace=False))
+    bt = inp.block_tables[0].cpu().numpy()[rows]
+    used = np.unique(bt[bt >= 0])
+    idx = torch.as_tensor(used, dtype=torch.long, device=inp.k_data.device)
+    host = [t.index_select(0, idx).cpu().numpy() for t in (inp.k_data, inp.k_scale, inp.extras["v_data"],
+                                                            inp.extras["v_scale"])]
+    remap = np.full(int(bt.max()) + 1, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    bt = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    qc = inp.q.cpu()[rows]
+    q = qc.view(torch.int16).numpy().view(np.uint16) if qc.dtype == torch.bfloat16 else qc.view(torch.uint8).numpy()
+    ctx = inp.seq_lens.cpu().numpy()[rows]
+    t0 = time.perf_counter()
+    attn.attn_decode(q=q, q_dtype=wl.q_dtype, k_data=host[0], k_scale=host[1], v_data=host[2], v_scale=host[3],
+                     block_table=bt, context_lens=ctx, page_size=wl.page_size, scale=float(np.float32(1 / np.sqrt(128))))
+    dt = time.perf_counter() - t0
+    trip = int(ctx.sum()) * wl.H * wl.attn_group
+    return {"value": trip / dt, "unit": "(row\u00d7head\u00d7token)/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.T} rows ({trip} live triples), {dt:.2f} s"}
 
 
 def cpu_baseline_select(wl, bs, inp, sample_rows: int):

@@ -277,6 +277,56 @@ int mxs_select_pages(int32_t mode, const mxs_batch* batch, int32_t num_heads, in
  * path and not capturable in a graph. Allocates host memory only. */
 int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* batch, int32_t check_scales, void* stream);
 
+/* ---------------------------------------------------------------- attention decode */
+
+/* One MXFP4 tensor (K or V) of a paged cache with kv heads, in two views:
+ *     data  byte e of token j, kv head hk, page p: data  + p*data_page_stride  + hk*data_head_stride  + j*64 + e
+ *     scale byte k of token j, kv head hk, page p: scale + p*scale_page_stride + hk*scale_head_stride + j*4  + k
+ * (the index cache's format per (page, kv head): element 2m in the low nibble
+ * of data byte m, scale byte k covering elements 32k..32k+31). data 16-byte
+ * aligned with strides multiples of 16; scale 4-byte aligned with strides
+ * multiples of 4. A single-region page [P x 64 B data][P x 4 B scales] per
+ * (page, kv head) is data = base, scale = base + 64 P with equal strides. */
+typedef struct mxs_kvview {
+  const void* data;
+  int64_t data_page_stride;    /* bytes */
+  int64_t data_head_stride;    /* bytes */
+  const void* scale;
+  int64_t scale_page_stride;   /* bytes */
+  int64_t scale_head_stride;   /* bytes */
+} mxs_kvview;
+
+typedef struct mxs_kvcache {
+  mxs_kvview k;
+  mxs_kvview v;
+  int32_t page_size;           /* 64 or 128 */
+  int32_t num_kv_heads;        /* >= 1 */
+  int64_t num_pages;           /* pages addressable through every view, >= 1 */
+} mxs_kvcache;
+
+/* Paged MXFP4 attention decode, one query row per row (ATOM #2770, "How it
+ * works" and the sparse attention commit: the selected pages' K and V are
+ * read as MXFP4 by a paged decode attention, one row per (token, kv head);
+ * the K/V format as above). For row r and query head h (kv head
+ * hk = h / G, G = q->num_heads / kv->num_kv_heads, 1 <= G <= 16) over the
+ * row's live tokens t < min(context_lens[r], max_context):
+ *     s_t = scale * (Q_hat[r, h] . K[t]),  out[r, h] = sum_t softmax(s)_t V[t]
+ * Q_hat is the query rounded as the scorers round it (bf16 -> e4m3, nearest
+ * even, saturating, unit scale; e4m3 used as stored). Token t of row r is in
+ * page block_table[r * bt_row_stride + t / P], slot t % P. Output: bf16
+ * [num_rows, Hq, 128], element (r, h, d) at out + (r * out_row_stride +
+ * h * out_head_stride + d) * 2 bytes (strides in elements, >= 0); a row with
+ * no live token gets zeros. Arithmetic: Q.K by the block-scaled MFMA (as in
+ * the scorers), softmax in fp32 (exp2), P rounded to bf16 and V widened to
+ * bf16 exactly for a bf16 MFMA with fp32 accumulation, one bf16 rounding of
+ * the normalized output. Device contract: block-table entries of live pages
+ * in [0, num_pages), e8m0 bytes of live tokens in [1, 254]. One kernel
+ * launch, no allocation, asynchronous on stream. Returns MXS_OK, MXS_EINVAL,
+ * MXS_EDTYPE, MXS_ELAYOUT, MXS_EUNSUPPORTED or MXS_EDEVICE. */
+int mxs_attn_decode(const mxs_query* q, const mxs_kvcache* kv, const int32_t* block_table, int64_t bt_row_stride,
+                    int32_t bt_width, const int32_t* context_lens, int32_t num_rows, int32_t max_context, float scale,
+                    void* out, int64_t out_row_stride, int64_t out_head_stride, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* mxs_last_error(void);
 

@@ -14,7 +14,8 @@ works"; aiter #5518, "Summary"):
 * :func:`score_logits` -- logits-first variant of prefill;
 * :func:`select_pages` -- top-k pages per (row, head) from block scores;
 * :func:`write_pages` -- quantize bf16 keys into their page slots;
-* :func:`check_metadata` -- synchronous check of the device-side contract.
+* :func:`check_metadata` -- synchronous check of the device-side contract;
+* :func:`attn_decode` -- paged MXFP4 attention decode over K and V caches.
 
 The cache is an MXFP4 one (``k_data`` [pages, P, 64] e2m1 bytes and
 ``k_scale`` [pages, P, 4] e8m0 bytes) or, with ``k_scale=None``, an fp8 one
@@ -33,7 +34,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["score_prefill", "score_decode", "score_logits", "select_pages", "write_pages", "check_metadata",
-           "make_plan", "library_path", "lib", "MxsError"]
+           "attn_decode", "make_plan", "library_path", "lib", "MxsError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxscore.so")
@@ -61,6 +62,17 @@ class KCache(ctypes.Structure):
                 ("num_pages", ctypes.c_int64)]
 
 
+class KVView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("data_page_stride", ctypes.c_int64), ("data_head_stride", ctypes.c_int64),
+                ("scale", ctypes.c_void_p), ("scale_page_stride", ctypes.c_int64),
+                ("scale_head_stride", ctypes.c_int64)]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("k", KVView), ("v", KVView), ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
+
+
 class Out(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("row_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
 
@@ -84,7 +96,8 @@ class Plan(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("mxs_plan_make", "mxs_plan_make_for", "mxs_score_prefill", "mxs_score_decode", "mxs_score_logits",
-           "mxs_write_pages", "mxs_select_pages", "mxs_check_metadata", "mxs_last_error", "mxs_version")
+           "mxs_write_pages", "mxs_select_pages", "mxs_check_metadata", "mxs_attn_decode", "mxs_last_error",
+           "mxs_version")
 
 
 def library_path() -> str:
@@ -116,6 +129,9 @@ def lib():
         L.mxs_write_pages.restype = ctypes.c_int
         L.mxs_check_metadata.argtypes = [i32, P(KCache), P(Batch), i32, ctypes.c_void_p]
         L.mxs_check_metadata.restype = ctypes.c_int
+        L.mxs_attn_decode.argtypes = [P(Query), P(KVCache), ctypes.c_void_p, i64, i32, ctypes.c_void_p, i32, i32,
+                                      ctypes.c_float, ctypes.c_void_p, i64, i64, ctypes.c_void_p]
+        L.mxs_attn_decode.restype = ctypes.c_int
         L.mxs_last_error.restype = ctypes.c_char_p
         L.mxs_last_error.argtypes = []
         L.mxs_version.restype = ctypes.c_char_p
@@ -390,3 +406,48 @@ def write_pages(k: torch.Tensor, slot_mapping: torch.Tensor, k_data, k_scale, st
     with torch.cuda.device(dev):
         _check(lib().mxs_write_pages(k.data_ptr(), k.stride(0), k.shape[0], slot_mapping.data_ptr(), ctypes.byref(kc),
                                      _stream(dev, stream)))
+
+
+def _kvview(data: torch.Tensor, scale: torch.Tensor, name: str) -> Tuple[KVView, Tuple[int, int, int]]:
+    """[pages, kv_heads, P, 64] e2m1 bytes + [pages, kv_heads, P, 4] e8m0 bytes."""
+    if data.dtype not in _DATA_DTYPES or scale.dtype not in _SCALE_DTYPES:
+        raise ValueError(f"{name} views must be uint8 (or fp4x2 / e8m0) tensors")
+    if data.dim() != 4 or scale.dim() != 4 or data.shape[3] != 64 or scale.shape[3] != 4 or \
+            tuple(data.shape[:3]) != tuple(scale.shape[:3]):
+        raise ValueError(f"{name} views must be [pages, kv_heads, P, 64] and [pages, kv_heads, P, 4], got "
+                         f"{tuple(data.shape)} / {tuple(scale.shape)}")
+    if data.stride(3) != 1 or data.stride(2) != 64 or scale.stride(3) != 1 or scale.stride(2) != 4:
+        raise ValueError(f"{name} token rows must be contiguous (64 B of data, 4 B of scales per token)")
+    return (KVView(data.data_ptr(), data.stride(0), data.stride(1), scale.data_ptr(), scale.stride(0), scale.stride(1)),
+            tuple(data.shape[:3]))
+
+
+def attn_decode(q: torch.Tensor, k_data, k_scale, v_data, v_scale, block_table: torch.Tensor, context_lens,
+                max_context: int, scale: float, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged MXFP4 attention decode: q [R, Hq, 128] (bf16 or e4m3), K and V caches
+    as [pages, Hkv, P, 64] + [pages, Hkv, P, 4] views, block_table [R, width],
+    context_lens [R] -> bf16 out [R, Hq, 128] (zeros for rows with no token)."""
+    dev = _same_device(q, k_data, k_scale, v_data, v_scale, block_table, context_lens, out)
+    qd = _query(q)
+    kview, kshape = _kvview(k_data, k_scale, "K")
+    vview, vshape = _kvview(v_data, v_scale, "V")
+    if kshape != vshape:
+        raise ValueError(f"K and V caches differ in shape: {kshape} vs {vshape}")
+    pages, Hkv, P = kshape
+    if P not in (64, 128):
+        raise ValueError(f"page size must be 64 or 128, got {P}")
+    R, Hq = q.shape[0], q.shape[1]
+    btp, bts, btw = _table(block_table)
+    if block_table.shape[0] < R:
+        raise ValueError("block_table has fewer rows than the query")
+    if out is None:
+        out = torch.empty((R, Hq, 128), dtype=torch.bfloat16, device=dev)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (R, Hq, 128) or out.stride(2) != 1:
+        raise ValueError(f"out must be bf16 [{R}, {Hq}, 128] with a contiguous last axis")
+    kv = KVCache(kview, vview, P, Hkv, pages)
+    with torch.cuda.device(dev):
+        _check(lib().mxs_attn_decode(ctypes.byref(qd), ctypes.byref(kv), btp, bts, btw,
+                                     _int_vec("context_lens", context_lens, R), R, int(max_context),
+                                     ctypes.c_float(scale), out.data_ptr(), out.stride(0), out.stride(1),
+                                     _stream(dev, stream)))
+    return out

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxscore.so")
 SOURCES = [os.path.join(CSRC, "mxs_api.cpp"), os.path.join(CSRC, "mxs_decode.hip"), os.path.join(CSRC, "mxs_prefill.hip"),
            os.path.join(CSRC, "mxs_logits.hip"), os.path.join(CSRC, "mxs_select.hip"),
-           os.path.join(CSRC, "mxs_write.hip")]
+           os.path.join(CSRC, "mxs_write.hip"), os.path.join(CSRC, "mxs_attn.hip")]
 HEADERS = [os.path.join(ROOT, "include", "mxscore.h"), os.path.join(CSRC, "mxs_internal.h"),
            os.path.join(CSRC, "mxs_device.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -340,6 +340,106 @@ int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, i
 
 const char* mxs_version(void) { return "mxscore 0.1 (gfx950)"; }
 
+int mxs_attn_decode(const mxs_query* q, const mxs_kvcache* kv, const int32_t* block_table, int64_t bt_row_stride,
+                    int32_t bt_width, const int32_t* context_lens, int32_t num_rows, int32_t max_context, float scale,
+                    void* out, int64_t out_row_stride, int64_t out_head_stride, void* stream) {
+  if (!q || !kv) return fail(MXS_EINVAL, "query and cache descriptors must not be NULL");
+  if (q->dtype != MXS_Q_BF16 && q->dtype != MXS_Q_E4M3)
+    return fail(MXS_EDTYPE, "query dtype must be bf16 (%d) or e4m3 (%d); got %d", MXS_Q_BF16, MXS_Q_E4M3, q->dtype);
+  if (kv->page_size != 64 && kv->page_size != 128)
+    return fail(MXS_ELAYOUT, "page_size must be 64 or 128, got %d", kv->page_size);
+  if (kv->num_kv_heads < 1 || q->num_heads < 1 || q->num_heads % kv->num_kv_heads)
+    return fail(MXS_EINVAL, "query heads (%d) must be a positive multiple of kv heads (%d)", q->num_heads,
+                kv->num_kv_heads);
+  const int32_t G = q->num_heads / kv->num_kv_heads;
+  if (G > 16) return fail(MXS_EUNSUPPORTED, "at most 16 query heads per kv head, got %d", G);
+  if (num_rows < 0 || max_context < 0) return fail(MXS_EINVAL, "num_rows and max_context must be >= 0");
+  if (!(std::isfinite(scale) && scale > 0.0f)) return fail(MXS_EINVAL, "scale must be finite and > 0");
+  if (num_rows == 0) return MXS_OK;
+  const int P = kv->page_size, Hkv = kv->num_kv_heads;
+  // query
+  const int64_t es = q->dtype == MXS_Q_BF16 ? 2 : 1;
+  if (!q->ptr) return fail(MXS_EINVAL, "query pointer is NULL");
+  if (!aligned(q->ptr, 16) || q->row_stride < 0 || q->head_stride < 0 || (q->row_stride * es) % 16 ||
+      (q->head_stride * es) % 16)
+    return fail(MXS_ELAYOUT, "query rows must be 16-byte aligned with strides in multiples of 16 bytes");
+  // cache views
+  auto check_view = [&](const char* name, const mxs_kvview& v) {
+    if (!v.data || !v.scale) return fail(MXS_EINVAL, "%s data and scale pointers must not be NULL", name);
+    if (!aligned(v.data, 16) || !aligned(v.scale, 4)) return fail(MXS_ELAYOUT, "%s views misaligned", name);
+    if (v.data_head_stride % 16 || v.data_page_stride % 16 || v.scale_head_stride % 4 || v.scale_page_stride % 4 ||
+        v.data_head_stride < 0 || v.scale_head_stride < 0)
+      return fail(MXS_ELAYOUT, "%s strides must be multiples of 16 (data) and 4 (scale) bytes", name);
+    if (Hkv > 1 && (v.data_head_stride < (int64_t)P * 64 || v.scale_head_stride < (int64_t)P * 4))
+      return fail(MXS_ELAYOUT, "%s head strides are narrower than a page of one head", name);
+    int64_t dspan, sspan;
+    if (!mul_add(Hkv - 1, v.data_head_stride, (int64_t)P * 64, &dspan) ||
+        !mul_add(Hkv - 1, v.scale_head_stride, (int64_t)P * 4, &sspan))
+      return fail(MXS_ELAYOUT, "%s span overflows", name);
+    if (kv->num_pages > 1 && (v.data_page_stride < dspan || v.scale_page_stride < sspan))
+      return fail(MXS_ELAYOUT, "%s page strides are narrower than a page of all kv heads", name);
+    int64_t tmp;
+    if (!mul_add(kv->num_pages, v.data_page_stride, dspan, &tmp) || !mul_add(kv->num_pages, v.scale_page_stride, sspan, &tmp))
+      return fail(MXS_ELAYOUT, "%s span overflows 64 bits", name);
+    return MXS_OK;
+  };
+  if (kv->num_pages < 1) return fail(MXS_EINVAL, "num_pages must be >= 1");
+  int rc = check_view("K", kv->k);
+  if (rc) return rc;
+  rc = check_view("V", kv->v);
+  if (rc) return rc;
+  // metadata and output
+  if (!block_table || !context_lens) return fail(MXS_EINVAL, "block_table and context_lens must not be NULL");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4)) return fail(MXS_ELAYOUT, "int32 metadata misaligned");
+  if (bt_width < ceil_div(max_context, P))
+    return fail(MXS_ELAYOUT, "block table width %d is narrower than ceil(max_context / page_size) = %lld", bt_width,
+                (long long)ceil_div(max_context, P));
+  if (num_rows > 1 && bt_row_stride < bt_width) return fail(MXS_ELAYOUT, "block table row stride below its width");
+  if (!out) return fail(MXS_EINVAL, "output pointer is NULL");
+  if (!aligned(out, 2) || out_row_stride < 0 || out_head_stride < 0)
+    return fail(MXS_ELAYOUT, "output must be 2-byte aligned with strides >= 0");
+  if (q->num_heads > 1 && out_head_stride < 128) return fail(MXS_ELAYOUT, "output head stride below 128 elements");
+  int64_t row_span;
+  if (!mul_add(q->num_heads - 1, out_head_stride, 128, &row_span) || (num_rows > 1 && out_row_stride < row_span))
+    return fail(MXS_ELAYOUT, "output row stride below one row");
+  if ((int64_t)num_rows * Hkv > INT32_MAX) return fail(MXS_EINVAL, "problem too large");
+  int dev;
+  DeviceInfo info;
+  rc = current_device(&dev, &info);
+  if (rc != MXS_OK) return rc;
+  mxs::AArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint8_t*>(q->ptr);
+  a.q_row_stride = q->row_stride * es;
+  a.q_head_stride = q->head_stride * es;
+  a.kd = static_cast<const uint8_t*>(kv->k.data);
+  a.kd_page_stride = kv->k.data_page_stride;
+  a.kd_head_stride = kv->k.data_head_stride;
+  a.ks = static_cast<const uint8_t*>(kv->k.scale);
+  a.ks_page_stride = kv->k.scale_page_stride;
+  a.ks_head_stride = kv->k.scale_head_stride;
+  a.vd = static_cast<const uint8_t*>(kv->v.data);
+  a.vd_page_stride = kv->v.data_page_stride;
+  a.vd_head_stride = kv->v.data_head_stride;
+  a.vs = static_cast<const uint8_t*>(kv->v.scale);
+  a.vs_page_stride = kv->v.scale_page_stride;
+  a.vs_head_stride = kv->v.scale_head_stride;
+  a.bt = block_table;
+  a.bt_stride = bt_row_stride;
+  a.ctx = context_lens;
+  a.R = num_rows;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.max_context = max_context;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out);
+  a.out_row_stride = out_row_stride;
+  a.out_head_stride = out_head_stride;
+  if (mxs::launch_attn(q->dtype, P, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(MXS_EDEVICE, "launching the attention decode failed: %s", hipGetErrorString(hipGetLastError()));
+  return MXS_OK;
+}
+
 // Pure planner: every input is a host integer; the same inputs give the same
 // plan. num_cus and wg_per_cu describe the device (CUs and resident
 // workgroups of the chosen kernel per CU).

@@ -104,7 +104,34 @@ struct WArgs {
   int32_t kdt;              // MXS_K_MXFP4 or MXS_K_E4M3
 };
 
+// Arguments of the attention-decode kernel (mxs_attn.hip).
+struct AArgs {
+  const uint8_t* q;
+  int64_t q_row_stride;     // bytes
+  int64_t q_head_stride;    // bytes
+  const uint8_t* kd;
+  int64_t kd_page_stride, kd_head_stride;   // bytes
+  const uint8_t* ks;
+  int64_t ks_page_stride, ks_head_stride;
+  const uint8_t* vd;
+  int64_t vd_page_stride, vd_head_stride;
+  const uint8_t* vs;
+  int64_t vs_page_stride, vs_head_stride;
+  const int32_t* bt;
+  int64_t bt_stride;        // elements
+  const int32_t* ctx;
+  int32_t R;                // rows
+  int32_t Hkv;
+  int32_t G;                // query heads per kv head, 1..16
+  int32_t max_context;
+  float scale_log2e;        // scale * log2(e): the softmax runs in exp2
+  uint16_t* out;            // bf16
+  int64_t out_row_stride;   // elements
+  int64_t out_head_stride;
+};
+
 // Launchers. Return the HIP status of the launch.
+hipError_t launch_attn(int32_t q_dtype, int32_t page_size, const AArgs& a, hipStream_t stream);
 hipError_t launch_select(int per, int64_t grid, const SArgs& a, hipStream_t stream);
 hipError_t launch_write(int64_t grid, const WArgs& a, hipStream_t stream);
 hipError_t launch_decode(const mxs_plan& plan, const KArgs& a, hipStream_t stream);

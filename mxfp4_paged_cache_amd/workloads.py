@@ -15,7 +15,9 @@ Recipe (the pages' scorer benchmarks use random K data with e8m0 bytes in
   per token drawn uniformly over the 254 finite e4m3 codes, no scale view;
 * block table: distinct pages drawn without replacement from a larger pool, so
   the gather is a real random gather;
-* cu_seqlens_q / seq_lens / prefix_lens: as the workload states.
+* cu_seqlens_q / seq_lens / prefix_lens: as the workload states;
+* attention decode (attn_group > 0): K and V caches [pages, kv heads, P, 64]
+  + [pages, kv heads, P, 4], bytes drawn as for the index cache.
 
 Streams: one torch.Generator per field, seeded with (seed, field id), so a
 field can be regenerated without the others.
@@ -60,6 +62,7 @@ class Workload:
     select_k: int = 0               # > 0: the workload is top-k page selection over this prefill's block scores
     write_tokens: int = 0           # > 0: the workload is writing this many bf16 keys into page slots
     k_dtype: str = "mxfp4"          # "mxfp4" (e2m1 + e8m0 views) | "e4m3" (fp8 cache, 128 B per token)
+    attn_group: int = 0             # > 0: paged attention decode; H kv heads with this many query heads each
     note: str = ""
 
     @property
@@ -124,12 +127,13 @@ class Inputs:
 def make_q(wl: Workload, seed: int, device="cpu", q_strided: bool = False) -> torch.Tensor:
     g = _gen(seed, F_Q, device)
     T = wl.T
-    x = torch.randn((T, wl.H, D), generator=g, device=device, dtype=torch.float32)
+    heads = wl.H * wl.attn_group if wl.attn_group else wl.H
+    x = torch.randn((T, heads, D), generator=g, device=device, dtype=torch.float32)
     dt = torch.bfloat16 if wl.q_dtype == "bf16" else torch.float8_e4m3fn
     if not q_strided:
         return x.to(dt)
     # strided rows: every row padded by 64 extra elements, heads padded by 128
-    big = torch.zeros((T, wl.H, 2 * D), device=device, dtype=dt)
+    big = torch.zeros((T, heads, 2 * D), device=device, dtype=dt)
     big[:, :, :D] = x.to(dt)
     return big[:, :, :D]
 
@@ -160,7 +164,15 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
         u = torch.randint(0, 254, shape, generator=gd, device=device, dtype=torch.uint8)
         return u + (u >= 0x7F).to(torch.uint8)
 
-    if wl.layout == "split":
+    if wl.attn_group:
+        # paged K and V caches with kv heads: [pool, H, P, 64] data + [pool, H, P, 4] scales each
+        k_data = torch.randint(0, 256, (pool, wl.H, P, SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
+        k_scale = torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, wl.H, P, SLOT_SCALE_BYTES), generator=gs,
+                                device=device, dtype=torch.uint8)
+        v_data = torch.randint(0, 256, (pool, wl.H, P, SLOT_DATA_BYTES), generator=gd, device=device, dtype=torch.uint8)
+        v_scale = torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, wl.H, P, SLOT_SCALE_BYTES), generator=gs,
+                                device=device, dtype=torch.uint8)
+    elif wl.layout == "split":
         k_data = data_bytes((pool, P, tb))
         k_scale = None if fp8 else torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, P, SLOT_SCALE_BYTES),
                                                  generator=gs, device=device, dtype=torch.uint8)
@@ -203,7 +215,9 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
     cu = [0]
     for ql in wl.q_lens:
         cu.append(cu[-1] + ql)
+    extras = {"v_data": v_data, "v_scale": v_scale} if wl.attn_group else {}
     return Inputs(
+        extras=extras,
         wl=wl,
         q=make_q(wl, seed, device, q_strided),
         k_data=k_data,
@@ -266,6 +280,14 @@ def write_1m_tokens() -> Workload:
                     seq_lens=[1], pool_pages=300_000, write_tokens=1 << 20)
 
 
+def attn_decode_sparse() -> Workload:
+    """Paged MXFP4 attention decode: 2048 rows (one kv head, 16 query heads each, e4m3 query), 2048 live
+    tokens per row (16 selected 128-token pages), K and V pages drawn from a 300k-page pool."""
+    return Workload("attn_decode_r2048_ctx2048_g16", "decode", H=1, page_size=128, q_lens=[1] * 2048,
+                    prefix_lens=[2047] * 2048, seq_lens=[2048] * 2048, q_dtype="e4m3", pool_pages=300_000,
+                    attn_group=16)
+
+
 def decode_b64_128k_fp8() -> Workload:
     """The decode workload over an fp8 (e4m3, 128 B per token) index cache: the format the MXFP4 one replaces."""
     wl = decode_b64_128k()
@@ -301,4 +323,5 @@ CONFIGS = {
     8: decode_b64_128k_fp8,
     9: prefill_long_fp8,
     10: write_1m_tokens_fp8,
+    11: attn_decode_sparse,
 }

@@ -69,7 +69,8 @@ def attn_decode(*, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale: np.
     k/v scale [pages, Hkv, P, 4] (uint8); block_table [R, width]; context_lens [R].
     Returns out [R', Hq, 128] float64 for the selected rows (all rows by default) and,
     with want_mag, mag [R', Hq, 128] = sum_t softmax(s)_t * |V_t| (the scale of the
-    output's rounding error)."""
+    output's rounding error) and qk_mag [R', Hq] = max_t sum_e |Q_hat_e K_t,e| (the
+    scale of a logit's rounding error)."""
     R, Hq, D = q.shape
     assert D == 128
     Hkv = k_data.shape[1]
@@ -80,6 +81,7 @@ def attn_decode(*, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale: np.
     sel = np.arange(R) if rows is None else np.asarray(rows)
     out = np.zeros((len(sel), Hq, 128), np.float64)
     mag = np.zeros((len(sel), Hq, 128), np.float64)
+    qk_mag = np.zeros((len(sel), Hq), np.float64)
     for n, r in enumerate(sel):
         ctx = int(context_lens[r])
         if ctx <= 0:
@@ -98,4 +100,5 @@ def attn_decode(*, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale: np.
             out[n, hk * G:(hk + 1) * G] = w @ V
             if want_mag:
                 mag[n, hk * G:(hk + 1) * G] = w @ np.abs(V)
-    return (out, mag) if want_mag else out
+                qk_mag[n, hk * G:(hk + 1) * G] = (np.abs(qg) @ np.abs(K).T).max(axis=1)
+    return (out, mag, qk_mag) if want_mag else out
