@@ -16,14 +16,18 @@
 //     probabilities are rounded to bf16, and the sum uses the rounded values
 //     so that the weights of the output stay a convex combination;
 //   * P.V: out^T[d][h] += V^T[d][t] P[t][h] with v_mfma_f32_16x16x32_bf16,
-//     32 tokens per step. A 32-token step takes the two Q.K tiles in the
-//     order k = 8g + u <-> token 4g + u (u < 4) of the first tile and
-//     4g + u - 4 of the second, so lane (g, i) already holds its P operand
-//     (head i, k = 8g..8g+7). V is widened to bf16 exactly with
+//     32 tokens per step. A 32-token step orders its tokens k = 8g + 2q + h
+//     <-> token 16h + 4g + q (h = 0, 1: the first or second Q.K tile), so
+//     lane (g, i) already holds its P operand (head i, k = 8g..8g+7), and
+//     tokens x and x + 16 sit at adjacent k: a lane that loads both (two
+//     contiguous 1 KB blocks per wave) writes their values for one head-dim
+//     element as one 4-byte word. V is widened to bf16 exactly with
 //     v_cvt_scalef32_pk_bf16_fp4 (e2m1 times a power of two is a bf16 value)
-//     and transposed through the wave's LDS tile [d][k] (80-byte rows: the
-//     16 lanes of a ds_read_b128 hit distinct banks). Dead tokens get a zero
-//     V scale and a -inf score, so their bytes cannot reach the output.
+//     and transposed through the wave's LDS tile [d][k]: 80-byte rows (the 16
+//     lanes of a ds_read_b128 hit distinct banks) and 64 more bytes before
+//     each group of 32 rows (the four rows one store instruction writes land
+//     in distinct banks). Dead tokens get a zero V scale and a -inf score, so
+//     their bytes cannot reach the output.
 #include "mxs_device.h"
 
 namespace mxs {
@@ -33,15 +37,15 @@ using namespace dev;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kVPitch = 40;                        // bf16 per row of the transposed V chunk
-constexpr int kVTileBytes = 128 * kVPitch * 2;     // one 32-token chunk, [128 d][40]
+constexpr int kVTileBytes = 128 * kVPitch * 2 + 3 * 64;   // one 32-token chunk, [128 d][40] + group offsets
 constexpr int kOPitch = 132;                       // floats per (wave, head) row of the merge area
 constexpr int kAttnLds = kWaves * kVTileBytes;     // also holds the merge area (4 x 16 x 132 floats)
 static_assert(kWaves * 16 * kOPitch * 4 <= kAttnLds, "merge area must fit in the V tiles");
 
 // K and V of one 64-token unit in registers (tokens slot0..slot0+63 of a
 // page). K tile t, lane (g, i): bytes 16g..16g+15 of token 16t+i and its e8m0
-// byte g. V chunk c (32 tokens), lane L: tokens 32c + 2m and 32c + 2m + 1
-// (m = L / 4), bytes 16(L % 4)..+15 of each (head dim 32(L % 4)..+31) and
+// byte g. V chunk c (32 tokens), lane L: tokens 32c + x and 32c + 16 + x
+// (x = L / 4), bytes 16(L % 4)..+15 of each (head dim 32(L % 4)..+31) and
 // their e8m0 byte L % 4.
 constexpr int kUnit = 64;
 struct AttnUnit {
@@ -63,19 +67,19 @@ __device__ __forceinline__ void load_attn_unit(AttnUnit& pg, const AArgs& a, int
     pg.kd[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(kd + (16 * t + i) * 64 + 16 * g));
     pg.ks[t] = __builtin_nontemporal_load(ks + (16 * t + i) * 4 + g);
   }
-  const int m = lane >> 2, pp = lane & 3;
+  const int x = lane >> 2, pp = lane & 3;
 #pragma unroll
   for (int c = 0; c < kUnit / 32; ++c) {
-    const int tok = 32 * c + 2 * m;
+    const int tok = 32 * c + x;
     pg.va[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vd + tok * 64 + 16 * pp));
-    pg.vb[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vd + (tok + 1) * 64 + 16 * pp));
+    pg.vb[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vd + (tok + 16) * 64 + 16 * pp));
     pg.vsa[c] = __builtin_nontemporal_load(vs + tok * 4 + pp);
-    pg.vsb[c] = __builtin_nontemporal_load(vs + (tok + 1) * 4 + pp);
+    pg.vsb[c] = __builtin_nontemporal_load(vs + (tok + 16) * 4 + pp);
   }
 }
 
-// k position of chunk-relative token x (0..31) in the P.V step
-__device__ __forceinline__ int k_of(int x) { return 8 * ((x & 15) >> 2) + (x >= 16 ? 4 : 0) + (x & 3); }
+// byte offset of element (d, k) of the transposed V tile
+__device__ __forceinline__ int vt_at(int d, int k) { return d * (kVPitch * 2) + 64 * (d >> 5) + 2 * k; }
 
 // The four bytes of src (8 e2m1 elements, element 2m in the low nibble of
 // byte m) times scale, as four packed bf16 pairs (pair m: elements 2m, 2m+1).
@@ -150,13 +154,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn(AArgs a) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db] *= alpha;
     // P.V, 32 tokens per step
-    const int m = lane >> 2, pp = lane & 3;
-    const int ka = k_of(2 * m);
+    const int x = lane >> 2, pp = lane & 3;
+    const int ka = 8 * (x >> 2) + 2 * (x & 3);   // k of token x; token x + 16 is at ka + 1
 #pragma unroll
     for (int c = 0; c < CPP; ++c) {
-      const int tok = j * kUnit + 32 * c + 2 * m;
+      const int tok = j * kUnit + 32 * c + x;
       const float sa = tok < ctx ? __builtin_bit_cast(float, (uint32_t)pg.vsa[c] << 23) : 0.0f;
-      const float sb = tok + 1 < ctx ? __builtin_bit_cast(float, (uint32_t)pg.vsb[c] << 23) : 0.0f;
+      const float sb = tok + 16 < ctx ? __builtin_bit_cast(float, (uint32_t)pg.vsb[c] << 23) : 0.0f;
       wave_lds_sync();   // the previous step's reads of vt are done
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -165,21 +169,20 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn(AArgs a) {
         fp4x8_to_bf16(pg.vb[c][w], sb, ub);
 #pragma unroll
         for (int bsel = 0; bsel < 4; ++bsel) {
-          // head-dim elements d0, d0 + 1 of tokens 2m (k = ka) and 2m + 1 (k = ka + 1)
+          // head-dim elements d0, d0 + 1 of tokens x (k = ka) and x + 16 (k = ka + 1)
           const int d0 = 32 * pp + 8 * w + 2 * bsel;
-          *reinterpret_cast<uint32_t*>(vt + (d0 * kVPitch + ka) * 2) =
-              __builtin_amdgcn_perm(ub[bsel], ua[bsel], 0x05040100u);
-          *reinterpret_cast<uint32_t*>(vt + ((d0 + 1) * kVPitch + ka) * 2) =
-              __builtin_amdgcn_perm(ub[bsel], ua[bsel], 0x07060302u);
+          *reinterpret_cast<uint32_t*>(vt + vt_at(d0, ka)) = __builtin_amdgcn_perm(ub[bsel], ua[bsel], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(vt + vt_at(d0 + 1, ka)) = __builtin_amdgcn_perm(ub[bsel], ua[bsel], 0x07060302u);
         }
       }
       wave_lds_sync();
-      const u4 pw = {pb[2 * c][0] | (pb[2 * c][1] << 16), pb[2 * c][2] | (pb[2 * c][3] << 16),
-                     pb[2 * c + 1][0] | (pb[2 * c + 1][1] << 16), pb[2 * c + 1][2] | (pb[2 * c + 1][3] << 16)};
+      // k = 8g + 2q + h: token 4g + q of tile 2c + h
+      const u4 pw = {pb[2 * c][0] | (pb[2 * c + 1][0] << 16), pb[2 * c][1] | (pb[2 * c + 1][1] << 16),
+                     pb[2 * c][2] | (pb[2 * c + 1][2] << 16), pb[2 * c][3] | (pb[2 * c + 1][3] << 16)};
       const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const u4 vw = *reinterpret_cast<const u4*>(vt + (16 * db + i) * (kVPitch * 2) + 16 * g);
+        const u4 vw = *reinterpret_cast<const u4*>(vt + vt_at(16 * db + i, 8 * g));
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pop, o[db], 0, 0, 0);
       }
     }
