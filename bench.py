@@ -108,7 +108,7 @@ def pmc_summary(dbs):
         for name, disp, val, kname in con.execute(
                 "select counter_name, dispatch_id, value, kernel_name from counters_collection"):
             kind = "copy" if "neg" in kname else next(
-                (k for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write") if k in kname), None)
+                (k for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write", "k_attn") if k in kname), None)
             if kind is None:
                 continue
             per.setdefault((name, kind), {}).setdefault(disp, 0.0)
@@ -118,7 +118,7 @@ def pmc_summary(dbs):
     out = {}
     for counter, field in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         copy = acc.get((counter, "copy"))
-        for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write"):
+        for k in ("k_decode", "k_prefill", "k_logits", "k_select", "k_write", "k_attn"):
             v = acc.get((counter, k))
             if v is None or not copy:
                 continue

@@ -309,3 +309,47 @@ def test_python_layer_fp8_cache_views():
         mx._kcache(torch.zeros((2, 64, 128), dtype=torch.bfloat16), None)         # not a byte view
     with pytest.raises(ValueError):
         mx._kcache(torch.zeros((2, 64, 256), dtype=torch.uint8)[:, :, :128], None)   # token rows not contiguous
+
+
+# ------------------------------------------------------------------ attention decode
+
+def attn_args():
+    q = mx.Query(FAKE, mx.MXS_Q_E4M3, 16 * 128, 128, 16)
+    kview = mx.KVView(FAKE + 0x100000, 8704, 8704, FAKE + 0x100000 + 8192, 8704, 8704)
+    vview = mx.KVView(FAKE + 0x900000, 8704, 8704, FAKE + 0x900000 + 8192, 8704, 8704)
+    kv = mx.KVCache(kview, vview, 128, 1, 100)
+    return q, kv
+
+
+def attn_call(L, q, kv, *, bt=FAKE + 0x2000000, bts=16, btw=16, ctx=FAKE + 0x3000000, R=8, maxc=2048, scale=0.088,
+              out=FAKE + 0x4000000, ors=16 * 128, ohs=128):
+    return L.mxs_attn_decode(ctypes.byref(q), ctypes.byref(kv), bt, bts, btw, ctx, R, maxc, ctypes.c_float(scale), out,
+                             ors, ohs, None)
+
+
+def test_attn_decode_rejections_before_device_work(L):
+    q, kv = attn_args()
+    assert attn_call(L, q, kv, R=0) == mx.MXS_OK                                        # nothing to do
+    cases = [
+        ("fp16 query", lambda q, kv: setattr(q, "dtype", 3), {}, mx.MXS_EDTYPE),
+        ("page size 32", lambda q, kv: setattr(kv, "page_size", 32), {}, mx.MXS_ELAYOUT),
+        ("heads not a multiple of kv heads", lambda q, kv: setattr(kv, "num_kv_heads", 3), {}, mx.MXS_EINVAL),
+        ("17 query heads per kv head", lambda q, kv: setattr(q, "num_heads", 17), {}, mx.MXS_EUNSUPPORTED),
+        ("zero scale", lambda q, kv: None, {"scale": 0.0}, mx.MXS_EINVAL),
+        ("misaligned K data", lambda q, kv: setattr(kv.k, "data", FAKE + 0x100008), {}, mx.MXS_ELAYOUT),
+        ("null V scale", lambda q, kv: setattr(kv.v, "scale", None), {}, mx.MXS_EINVAL),
+        ("narrow K page stride", lambda q, kv: setattr(kv.k, "data_page_stride", 4096), {}, mx.MXS_ELAYOUT),
+        ("narrow block table", lambda q, kv: None, {"btw": 15}, mx.MXS_ELAYOUT),
+        ("null context lengths", lambda q, kv: None, {"ctx": None}, mx.MXS_EINVAL),
+        ("narrow output rows", lambda q, kv: None, {"ors": 128}, mx.MXS_ELAYOUT),
+        ("null output", lambda q, kv: None, {"out": None}, mx.MXS_EINVAL),
+        ("misaligned query", lambda q, kv: setattr(q, "ptr", FAKE + 8), {}, mx.MXS_ELAYOUT),
+    ]
+    for name, mutate, kw, code in cases:
+        q, kv = attn_args()
+        mutate(q, kv)
+        assert attn_call(L, q, kv, **kw) == code, (name, L.mxs_last_error())
+    import torch
+    if torch.cuda.device_count() == 0:
+        q, kv = attn_args()
+        assert attn_call(L, q, kv) == mx.MXS_EUNSUPPORTED                               # valid: stops at the device
