@@ -187,12 +187,14 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
         if (sel) { if (lane == 0) sel[0] = tail; } else if (lane == 0) orow[0] = tail;
         written = 1;
       } else {
-        // lower bound x of T: the smallest second-largest or largest lane key
-        // (valid when keff <= 2 n2 or <= n1 lanes hold one), else none
+        // lower bound x of T: the smallest largest lane key when keff <= n1
+        // lanes hold one (each of them holds a key >= it), else the smallest
+        // second-largest lane key when keff <= 2 n2, else none. The first is
+        // the tighter (x1 >= x2): fewer candidates and fewer bits to search.
         const uint32_t n1 = ballot_count(t1 != 0u), n2 = ballot_count(t2 != 0u);
         const uint32_t x2 = wave_min(t2 != 0u ? t2 : 0xFFFFFFFFu);
         const uint32_t x1 = wave_min(t1 != 0u ? t1 : 0xFFFFFFFFu);
-        const uint32_t x = keff <= 2 * n2 ? x2 : (keff <= n1 ? x1 : 1u);
+        const uint32_t x = keff <= n1 ? x1 : (keff <= 2 * n2 ? x2 : 1u);
         const uint32_t K = wave_max(kmax);
         const uint32_t diff = x ^ K;
         const int nbits = diff ? 32 - __builtin_clz(diff) : 0;
