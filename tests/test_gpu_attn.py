@@ -175,3 +175,62 @@ def test_full_attention_workload_sampled_rows():
     compare(out.float().cpu().numpy()[rows], ref, mag, qkm, "attention workload (4 sampled rows)")
     del out, inp
     torch.cuda.empty_cache()
+
+
+def test_sparse_pipeline_graph_replay_with_poisoned_outputs():
+    # decode scores over an fp8 index cache -> top-k pages of head 0 -> the
+    # selected pages' K and V through the attention decode, captured in one
+    # HIP graph; outputs are poisoned (NaN / -7) before every replay, and
+    # every replay must give the eager result bit for bit
+    P, B, k = 128, 4, 8
+    wl = W.Workload("g_sparse", "decode", H=64, page_size=P, q_lens=[1] * B, prefix_lens=[0] * B,
+                    seq_lens=[3000, 700, 129, 2000], k_dtype="e4m3", max_seq_len=3072)
+    dev = W.make_inputs(wl, 44, "cuda")
+    NB = wl.NB
+    pool = dev.k_data.shape[0]
+    rng = np.random.default_rng(45)
+    kv = [torch.from_numpy(a).cuda() for a in (rng.integers(0, 256, (pool, 1, P, 64), dtype=np.uint8),
+                                                 rng.integers(122, 128, (pool, 1, P, 4), dtype=np.uint8),
+                                                 rng.integers(0, 256, (pool, 1, P, 64), dtype=np.uint8),
+                                                 rng.integers(122, 128, (pool, 1, P, 4), dtype=np.uint8))]
+    qa = torch.randn((B, 16, 128), device="cuda").to(torch.bfloat16)
+    bs = torch.empty((B, 64, NB), device="cuda")
+    sel = torch.empty((B, 64, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda")
+    plan = mx.make_plan("decode", torch.bfloat16, P, 64, B, 1, wl.window, False, True, k_dtype="e4m3")
+    seq = dev.seq_lens
+    tail_tokens = ((seq - 1) % P + 1).to(torch.int32)
+
+    def step():
+        mx.score_decode(dev.q, dev.k_data, None, dev.block_table, seq, wl.window, SCALE, out=bs, plan=plan)
+        mx.select_pages(bs, k, seq, wl.window, P, out=sel)
+        s0 = sel[:, 0, :]
+        live = s0 >= 0
+        table = torch.where(live, dev.block_table.gather(1, s0.clamp(min=0).long()), -1).to(torch.int32)
+        ctx = ((live.sum(1).to(torch.int32) - 1) * P + tail_tokens).to(torch.int32)
+        mx.attn_decode(qa, kv[0], kv[1], kv[2], kv[3], table.contiguous(), ctx.contiguous(), k * P, SCALE, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [bs.clone(), sel.clone(), out.clone()]
+    assert torch.isfinite(out.float()).all()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        bs.fill_(float("nan"))
+        sel.fill_(-7)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bs.view(torch.int32), eager[0].view(torch.int32)), rep
+        assert torch.equal(sel, eager[1]), rep
+        assert torch.equal(out.view(torch.int16), eager[2].view(torch.int16)), rep
+    say("  3 replays of score -> select -> attention with poisoned outputs equal the eager run")
