@@ -39,24 +39,29 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, d));
-  return x;
+// Wave-wide min / max as a uniform value, with DPP row shifts (lane i takes
+// lane i - n of its 16-lane row; lanes with no source keep the identity),
+// then the row-15 and row-31 broadcasts: lane 63 ends with the result.
+template <bool MIN>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+  constexpr int id = MIN ? -1 : 0;   // identity: 0xFFFFFFFF for min, 0 for max
+  auto op = [](uint32_t a, uint32_t b) { return MIN ? min(a, b) : max(a, b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, d));
-  return x;
-}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) { return wave_reduce<true>(x); }
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) { return wave_reduce<false>(x); }
 
 // The scores of one (row, head), all loads issued together (indices past NB
 // read the last page's score and are then dropped, so no load is predicated).
 template <int PER>
-__device__ __forceinline__ void load_scores(const SArgs& a, int64_t item, int lane, float (&v)[PER]) {
-  const int64_t r = item / a.H;
-  const int h = (int)(item - r * a.H);
+__device__ __forceinline__ void load_scores(const SArgs& a, int64_t r, int h, int lane, float (&v)[PER]) {
   const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
 #pragma unroll
   for (int m = 0; m < PER; ++m) v[m] = srow[min(64 * m + lane, a.NB - 1)];
@@ -131,16 +136,32 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
   uint32_t* ck = cand_keys[wv];
   int32_t* ci = cand_idx[wv];
   int32_t* sel = a.k <= kSelectStage ? sel_all[wv] : nullptr;
+  // Item = row * H + head. The grid stride nw is fixed, so (row, head) is
+  // advanced by (nw / H, nw % H) with a carry instead of dividing per item
+  // (a 64-bit division is a long scalar sequence).
+  const int64_t step_r = nw / a.H;
+  const int step_h = (int)(nw - step_r * a.H);
+  int64_t nr = wave / a.H;
+  int nh = (int)(wave - nr * a.H);
+  auto advance = [&]() {
+    nh += step_h;
+    nr += step_r;
+    if (nh >= a.H) {
+      nh -= a.H;
+      ++nr;
+    }
+  };
   // the next item's scores are in flight while this one is selected
   float nxt[PER];
-  if (wave < a.items) load_scores<PER>(a, wave, lane, nxt);
+  if (wave < a.items) load_scores<PER>(a, nr, nh, lane, nxt);
   for (int64_t item = wave; item < a.items; item += nw) {
     float cur[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) cur[m] = nxt[m];
-    if (item + nw < a.items) load_scores<PER>(a, item + nw, lane, nxt);
-    const int64_t r = item / a.H;
-    const int h = (int)(item - r * a.H);
+    const int64_t r = nr;
+    const int h = nh;
+    advance();
+    if (item + nw < a.items) load_scores<PER>(a, nr, nh, lane, nxt);
     // the row's visible tokens, as the scorer masks them
     int lim;
     if (a.decode) {
@@ -156,6 +177,12 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
     lim = clampi(lim, 0, a.max_seq_len);
     const int tail = lim > 0 ? (lim - 1) / a.P : -1;
 
+    // The window width is opaque to the optimizer here: hoisted out of the
+    // item loop, the PER page-in-window lane masks would not fit the scalar
+    // registers and would be spilled and reloaded for every item, which costs
+    // more than comparing again.
+    int nb = a.NB;
+    asm volatile("" : "+s"(nb));
     uint32_t key[PER];
     int32_t idx[PER];
     uint32_t t1 = 0, t2 = 0, kmax = 0;   // the lane's two largest keys; its largest non-tail key
@@ -165,7 +192,7 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
       const int j = 64 * m + lane;
       idx[m] = j;
       const uint32_t bits = __float_as_uint(cur[m]);
-      const bool live = j < a.NB && (bits & 0x7F800000u) != 0x7F800000u;   // finite score
+      const bool live = j < nb && (bits & 0x7F800000u) != 0x7F800000u;   // finite score
       const bool is_tail = live && j == tail;
       tail_here |= is_tail;
       key[m] = live ? (is_tail ? 0xFFFFFFFFu : order_key(cur[m])) : 0u;
