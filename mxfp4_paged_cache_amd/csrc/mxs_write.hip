@@ -36,6 +36,8 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
   const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t nw = (int64_t)gridDim.x * kWaves;
   const int64_t quads = (a.n + 3) / 4;
+  // page size 64 or 128 (checked on the host): slot -> (page, offset) by shift and mask
+  const int psh = a.P == 128 ? 7 : 6;
   for (int64_t w = w0; w * kWriteSteps < quads; w += nw) {
     int64_t slot[kWriteSteps], page[kWriteSteps];
     bool ok[kWriteSteps];
@@ -45,7 +47,7 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
       const int64_t t = 4 * (w * kWriteSteps + u) + sub;
       const bool tok = t < a.n;
       slot[u] = tok ? a.slots[t] : -1;
-      page[u] = slot[u] >= 0 ? slot[u] / a.P : -1;
+      page[u] = slot[u] >= 0 ? slot[u] >> psh : -1;
       ok[u] = tok && slot[u] >= 0 && page[u] < a.num_pages;   // slots outside the pool are skipped
       // 8 bf16 elements (16 bytes); a skipped token reads row 0, which exists
       raw[u] = *reinterpret_cast<const uint4*>(a.k + (ok[u] ? t : 0) * a.k_row_stride + 8 * l);
@@ -57,7 +59,7 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
         // fp8 cache: elements 8 l .. 8 l + 7 as e4m3 bytes, in element order
         const uint2 v = {(uint32_t)bf16x4_to_e4m3(w4[0], w4[1]), (uint32_t)bf16x4_to_e4m3(w4[2], w4[3])};
         if (ok[u]) {
-          const int64_t off = slot[u] - page[u] * a.P;
+          const int64_t off = slot[u] & (a.P - 1);
           *reinterpret_cast<uint2*>(a.kd + page[u] * a.kd_page_stride + off * 128 + 8 * l) = v;
         }
         continue;
@@ -84,7 +86,7 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, x[4], x[5], sc, 2);
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, x[6], x[7], sc, 3);
       if (ok[u]) {
-        const int64_t off = slot[u] - page[u] * a.P;
+        const int64_t off = slot[u] & (a.P - 1);
         *reinterpret_cast<uint32_t*>(a.kd + page[u] * a.kd_page_stride + off * 64 + 4 * l) = packed;
         if ((l & 3) == 0) a.ks[page[u] * a.ks_page_stride + off * 4 + (l >> 2)] = (uint8_t)byte;
       }
