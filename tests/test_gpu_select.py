@@ -70,6 +70,23 @@ def test_decode_rows_and_strided_views(P):
     assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, 6))
 
 
+def test_many_items_per_wave_odd_head_count():
+    # More (row, head) items than the grid has waves (the grid is capped at
+    # 32 workgroups per CU), with 7 heads, which do not divide the grid
+    # stride: each wave takes several items and the head index wraps when
+    # the stride is added.
+    P, NB, H, R = 64, 9, 7, 10000
+    rng = np.random.default_rng(77)
+    msl = NB * P
+    seq = rng.integers(0, msl + 1, R)
+    lim = topk.row_limits("decode", seq, msl)
+    s = synthetic_scores(rng, lim, H, P, NB)
+    say(f"decode select rows={R} heads={H} k=4")
+    got = mx.select_pages(torch.from_numpy(s).cuda(), 4, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, 4))
+
+
 def test_selection_of_scorer_output():
     # the step as it follows the scorer: block scores of the 64-row prefill
     # workload (ctx 1024, 8 pages), k = 3
