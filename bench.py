@@ -199,8 +199,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the scorer needs no "
-              f"collective; see DESIGN.md for how the path shards)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported. The scorer needs no "
+              f"collective: every output element depends on one query vector and one token's K, so requests, "
+              f"heads or context pages split across GPUs with no exchange step", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
