@@ -54,19 +54,17 @@ __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[
       m[n] = max_into(m[n], c);
     }
   };
-  // two tiles per trip, no MFMA result carried across trips; the next pair of
-  // K tiles is read from LDS while this pair is multiplied and folded
-  KTile<KDT> k0 = lds_tile<KDT, P>(kb, g, i, 0);
-  KTile<KDT> k1 = lds_tile<KDT, P>(kb, g, i, 1);
+  // Two tiles per trip and nothing carried across trips: the trip's K tiles
+  // are read from LDS at its top (the other wave on the SIMD covers the LDS
+  // latency). Prefetching the next pair into the loop-carried registers
+  // instead cost one register copy per two MFMAs and measured 2% slower.
 #pragma unroll 1
   for (int t = 0; t < TPP; t += 2) {
+    const KTile<KDT> k0 = lds_tile<KDT, P>(kb, g, i, t);
+    const KTile<KDT> k1 = lds_tile<KDT, P>(kb, g, i, t + 1);
     v4f cA[NQ], cB[NQ];
     mma(k0, cA);
     mma(k1, cB);
-    if (t + 2 < TPP) {
-      k0 = lds_tile<KDT, P>(kb, g, i, t + 2);
-      k1 = lds_tile<KDT, P>(kb, g, i, t + 3);
-    }
     fold(t, cA);
     fold(t + 1, cB);
   }
