@@ -28,6 +28,10 @@ using namespace dev;
 // maximum takes two lane exchanges). A wave takes kWriteSteps steps at once,
 // all loads first, so that enough bytes are in flight to cover the latency.
 constexpr int kWriteSteps = 4;
+// The cache bytes are stored non-temporally (they are not read back soon):
+// 2^20 keys took 59 us against 71.5 us with ordinary stores on one MI355X.
+// The keys themselves are read with ordinary loads (non-temporal loads as
+// well measured slower than either alone).
 
 template <int KDT>
 __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
@@ -60,7 +64,9 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
         const uint2 v = {(uint32_t)bf16x4_to_e4m3(w4[0], w4[1]), (uint32_t)bf16x4_to_e4m3(w4[2], w4[3])};
         if (ok[u]) {
           const int64_t off = slot[u] & (a.P - 1);
-          *reinterpret_cast<uint2*>(a.kd + page[u] * a.kd_page_stride + off * 128 + 8 * l) = v;
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(u2{v.x, v.y},
+                                      reinterpret_cast<u2*>(a.kd + page[u] * a.kd_page_stride + off * 128 + 8 * l));
         }
         continue;
       }
@@ -87,8 +93,9 @@ __global__ void __launch_bounds__(kThreads) k_write(WArgs a) {
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, x[6], x[7], sc, 3);
       if (ok[u]) {
         const int64_t off = slot[u] & (a.P - 1);
-        *reinterpret_cast<uint32_t*>(a.kd + page[u] * a.kd_page_stride + off * 64 + 4 * l) = packed;
-        if ((l & 3) == 0) a.ks[page[u] * a.ks_page_stride + off * 4 + (l >> 2)] = (uint8_t)byte;
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(a.kd + page[u] * a.kd_page_stride + off * 64 + 4 * l));
+        if ((l & 3) == 0)
+          __builtin_nontemporal_store((uint8_t)byte, a.ks + page[u] * a.ks_page_stride + off * 4 + (l >> 2));
       }
     }
   }
