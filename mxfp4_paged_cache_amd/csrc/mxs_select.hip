@@ -81,6 +81,61 @@ __device__ __forceinline__ uint32_t search_threshold(const uint32_t (&k)[N], uin
   return T;
 }
 
+// Inclusive prefix sum over the wave's lanes (DPP row shifts, then the
+// row-15 and row-31 broadcasts carry each row's total into the next rows).
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+// The same threshold as search_threshold (the largest T with
+// count(keys >= T) >= keff), found 6 bits per round: the keys that share T's
+// bits fixed so far are counted per next digit in the wave's LDS histogram
+// (64 bins, LDS atomics), and the digit is the largest whose count, with
+// every key already above, reaches keff. Lane l reads the bin of digit
+// 63 - l, so an inclusive scan over the lanes counts the keys at or above
+// each digit, and the first lane where that reaches keff names it. Zero keys
+// (empty slots) are never counted. Against the bitwise search (one round per
+// bit, about 24 here) this took the top-64 selection over 4096 x 64 x 1024
+// block scores from 571 us to 509 us on one MI355X (8-bit digits: 521 us).
+template <int N>
+__device__ __forceinline__ uint32_t radix_threshold(const uint32_t (&k)[N], uint32_t T0, int nbits, uint32_t keff,
+                                                    uint32_t* hist, int lane) {
+  uint32_t above = 0;   // keys above every value the search can still reach
+  if (nbits < 32) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) above += ballot_count((k[q] >> nbits) > (T0 >> nbits));
+  }
+  uint32_t prefix = T0;
+  for (int rem = nbits; rem > 0;) {
+    const int w = rem < 6 ? rem : 6;
+    const int sh = rem - w;
+    wave_lds_sync();   // the last round's reads of the histogram are done
+    hist[lane] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const uint32_t kq = k[q];
+      const bool match = kq != 0u && (rem == 32 || (kq >> rem) == (prefix >> rem));
+      if (match) atomicAdd(hist + ((kq >> sh) & ((1u << w) - 1u)), 1u);
+    }
+    wave_lds_sync();
+    const uint32_t hv = hist[63 - lane];   // lane l: digit 63 - l
+    const uint32_t incl = wave_scan(hv);
+    const uint64_t hit = __ballot(above + incl >= keff);
+    const int L = (int)__builtin_ctzll(hit);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)(above + incl - hv), L);
+    prefix |= (uint32_t)(63 - L) << sh;
+    rem = sh;
+  }
+  return prefix;
+}
+
 // Emit, in page order, the keys above T and the first need_eq keys equal to
 // T: page ids go to sel[] (LDS) while k fits, else straight to the output row.
 template <int N>
@@ -107,7 +162,7 @@ constexpr int kSelectCand = 512;   // candidates per (row, head) the pruned sear
 template <int NC>
 __device__ __forceinline__ uint32_t select_candidates(const uint32_t* ck, const int32_t* ci, uint32_t ncand, int lane,
                                                       uint32_t T0, int nbits, uint32_t keff, int32_t* sel,
-                                                      int32_t* orow) {
+                                                      int32_t* orow, uint32_t* hist) {
   uint32_t k2[NC];
   int32_t i2[NC];
 #pragma unroll
@@ -116,7 +171,7 @@ __device__ __forceinline__ uint32_t select_candidates(const uint32_t* ck, const 
     k2[q] = c < ncand ? ck[c] : 0u;
     i2[q] = c < ncand ? ci[c] : 0;
   }
-  const uint32_t T = search_threshold(k2, T0, nbits, keff);
+  const uint32_t T = radix_threshold(k2, T0, nbits, keff, hist, lane);
   uint32_t gt = 0;
 #pragma unroll
   for (int q = 0; q < NC; ++q) gt += ballot_count(k2[q] > T);
@@ -129,6 +184,7 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
   __shared__ uint32_t cand_keys[kWaves][kSelectCand];
   __shared__ int32_t cand_idx[kWaves][kSelectCand];
   __shared__ int32_t sel_all[kWaves][kSelectStage];
+  __shared__ uint32_t hist_all[kWaves][64];   // radix threshold histogram
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t wave = (int64_t)blockIdx.x * kWaves + wv;
@@ -246,11 +302,11 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           // the candidates back in registers, as few per lane as they need
           if (ncand <= 128)
-            written = select_candidates<2>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+            written = select_candidates<2>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow, hist_all[wv]);
           else if (ncand <= 256)
-            written = select_candidates<4>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+            written = select_candidates<4>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow, hist_all[wv]);
           else
-            written = select_candidates<8>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow);
+            written = select_candidates<8>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow, hist_all[wv]);
         } else {
           const uint32_t T = search_threshold(key, T0, nbits, keff);
           uint32_t gt = 0;
