@@ -20,7 +20,7 @@ using namespace dev;
 // (-inf) get key 0 and the tail page the largest key, so it is always chosen.
 // The result is every page whose key exceeds T, the k-th largest key (k
 // clipped to the live pages), and the lowest-indexed pages whose key equals
-// T, emitted in page order. T comes from a greedy bitwise search:
+// T, emitted in page order. T comes from a radix search (6 bits per round):
 //   * pruning: if each of n lanes holds j keys >= some x, then n j keys are
 //     >= x; with x the smallest such j-th lane key (j = 2 or 1) and k <= n j,
 //     T >= x, so only keys >= x are candidates; they are compacted in page
@@ -67,20 +67,6 @@ __device__ __forceinline__ void load_scores(const SArgs& a, int64_t r, int h, in
   for (int m = 0; m < PER; ++m) v[m] = srow[min(64 * m + lane, a.NB - 1)];
 }
 
-// Greedy search for the largest T with count(keys >= T) >= keff, over the
-// bits below the first nbits; T starts from those leading bits.
-template <int N>
-__device__ __forceinline__ uint32_t search_threshold(const uint32_t (&k)[N], uint32_t T, int nbits, uint32_t keff) {
-  for (int bit = nbits - 1; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int q = 0; q < N; ++q) cnt += ballot_count(k[q] >= cand);
-    if (cnt >= keff) T = cand;
-  }
-  return T;
-}
-
 // Inclusive prefix sum over the wave's lanes (DPP row shifts, then the
 // row-15 and row-31 broadcasts carry each row's total into the next rows).
 __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
@@ -93,16 +79,17 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
   return x;
 }
 
-// The same threshold as search_threshold (the largest T with
-// count(keys >= T) >= keff), found 6 bits per round: the keys that share T's
+// The largest T with count(keys >= T) >= keff, over the bits below the first
+// 32 - nbits (T starts from those leading bits), found 6 bits per round: the keys that share T's
 // bits fixed so far are counted per next digit in the wave's LDS histogram
 // (64 bins, LDS atomics), and the digit is the largest whose count, with
 // every key already above, reaches keff. Lane l reads the bin of digit
 // 63 - l, so an inclusive scan over the lanes counts the keys at or above
 // each digit, and the first lane where that reaches keff names it. Zero keys
-// (empty slots) are never counted. Against the bitwise search (one round per
-// bit, about 24 here) this took the top-64 selection over 4096 x 64 x 1024
-// block scores from 571 us to 509 us on one MI355X (8-bit digits: 521 us).
+// (empty slots) are never counted. Against a bitwise search (one ballot round
+// per bit, about 24 here) this took the top-64 selection over 4096 x 64 x
+// 1024 block scores from 571 us to 509 us on one MI355X (8-bit digits:
+// 521 us).
 template <int N>
 __device__ __forceinline__ uint32_t radix_threshold(const uint32_t (&k)[N], uint32_t T0, int nbits, uint32_t keff,
                                                     uint32_t* hist, int lane) {
@@ -308,7 +295,7 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
           else
             written = select_candidates<8>(ck, ci, ncand, lane, T0, nbits, keff, sel, orow, hist_all[wv]);
         } else {
-          const uint32_t T = search_threshold(key, T0, nbits, keff);
+          const uint32_t T = radix_threshold(key, T0, nbits, keff, hist_all[wv], lane);
           uint32_t gt = 0;
 #pragma unroll
           for (int m = 0; m < PER; ++m) gt += ballot_count(key[m] > T);
