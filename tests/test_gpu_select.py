@@ -54,6 +54,26 @@ def test_prefill_rows_match_oracle(NB, k):
     assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
 
 
+@pytest.mark.parametrize("NB,k", [(2100, 300), (4096, 600)])
+def test_large_k(NB, k):
+    # k above the 256 results staged in LDS: ids go straight to the output
+    # row; with more than 512 candidates the search runs without compaction
+    P = 64
+    rng = np.random.default_rng(NB + k)
+    q_lens, prefix = [2, 3], [NB * P - 2, NB * P // 3]
+    seq = [min(p + q, NB * P) for p, q in zip(prefix, q_lens)]
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    msl = NB * P
+    lim = topk.row_limits("prefill", seq, msl, cu, prefix)
+    s = synthetic_scores(rng, lim, 2, P, NB, n_values=7)
+    say(f"prefill select NB={NB} k={k} rows={len(lim)}")
+    got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P,
+                          cu_seqlens_q=torch.from_numpy(cu).cuda(),
+                          prefix_lens=torch.tensor(prefix, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
+
+
 @pytest.mark.parametrize("P", [64, 128])
 def test_decode_rows_and_strided_views(P):
     rng = np.random.default_rng(P)
