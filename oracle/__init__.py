@@ -102,6 +102,9 @@ def lib():
                                              ctypes.c_int, ctypes.c_float]
         L.mxo_score.restype = ctypes.c_int
         L.mxo_score.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mxo_score_ex.restype = ctypes.c_int
+        L.mxo_score_ex.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
         L.mxo_total_rows.restype = ctypes.c_int
         L.mxo_total_rows.argtypes = [ctypes.POINTER(_Args)]
         _lib = L
@@ -153,6 +156,7 @@ class Result:
     blocks: Optional[np.ndarray]   # [R, H, NB] fp32
     mags: Optional[np.ndarray]     # [R, H, max_seq_len] float64: sum |Q_hat * K| (no sm_scale)
     rows: np.ndarray               # the query rows these outputs belong to
+    block_mags: Optional[np.ndarray] = None   # [R, H, NB] float64: largest mags among a page's live tokens
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -164,6 +168,7 @@ def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale
           sm_scale: float, cu_seqlens_q: Optional[np.ndarray] = None,
           prefix_lens: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
           want_logits: bool = True, want_blocks: bool = True, want_mags: bool = False,
+          want_block_mags: bool = False,
           data_page_stride: Optional[int] = None, scale_page_stride: Optional[int] = None,
           num_pages: Optional[int] = None, num_threads: int = 0, k_dtype: str = "mxfp4") -> Result:
     """Run the C oracle on host arrays.
@@ -233,8 +238,9 @@ def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale
     lg = np.empty((R, H, max_seq_len), np.float32) if want_logits else None
     bl = np.empty((R, H, NB), np.float32) if want_blocks else None
     mg = np.empty((R, H, max_seq_len), np.float64) if want_mags else None
-    rc = lib().mxo_score(ctypes.byref(a), _ptr(lg), _ptr(bl), _ptr(mg))
+    bm = np.empty((R, H, NB), np.float64) if want_block_mags else None
+    rc = lib().mxo_score_ex(ctypes.byref(a), _ptr(lg), _ptr(bl), _ptr(mg), _ptr(bm))
     del keep
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
-    return Result(lg, bl, mg, rows_arr)
+    return Result(lg, bl, mg, rows_arr, bm)

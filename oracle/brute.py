@@ -128,17 +128,41 @@ def token_k_e4m3(data_page: bytes, slot: int) -> List[Optional[Fraction]]:
     return [e4m3(data_page[slot * 128 + e]) for e in range(128)]
 
 
+def token_mag(qh: List[Fraction], data_page: bytes, scale_page: bytes, slot: int) -> Fraction:
+    """M of one (query vector, token) pair: sum over the 128 elements of
+    |Q_hat[e]| * |e2m1(code e)| * 2^(scale byte - 127), the magnitude of the
+    terms the dot adds up (no sm_scale). Live tokens only (no NaN scale)."""
+    total = Fraction(0)
+    for e in range(128):
+        byte = data_page[slot * 64 + e // 2]
+        code = (byte >> 4) if e % 2 else (byte & 0xF)
+        total += abs(qh[e]) * abs(e2m1(code)) * e8m0(scale_page[slot * 4 + e // 32])
+    return total
+
+
 def score(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size: int,
           block_table, seq_lens, max_seq_len: int, sm_scale: float, cu_seqlens_q=None,
           prefix_lens=None, k_dtype: str = "mxfp4"):
+    """(logits, blocks) of :func:`score_mags`."""
+    lg, bl, _ = score_mags(mode=mode, q_rows=q_rows, q_dtype=q_dtype, pages_data=pages_data,
+                           pages_scale=pages_scale, page_size=page_size, block_table=block_table,
+                           seq_lens=seq_lens, max_seq_len=max_seq_len, sm_scale=sm_scale,
+                           cu_seqlens_q=cu_seqlens_q, prefix_lens=prefix_lens, k_dtype=k_dtype)
+    return lg, bl
+
+
+def score_mags(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size: int,
+               block_table, seq_lens, max_seq_len: int, sm_scale: float, cu_seqlens_q=None,
+               prefix_lens=None, k_dtype: str = "mxfp4"):
     """Brute force over every (row, head, token).
 
     ``q_rows[r][h]`` is a list of 128 ints (bf16 bits or e4m3 bytes);
     ``pages_data[p]``/``pages_scale[p]`` are bytes objects of P*64 / P*4 bytes
     (k_dtype "mxfp4"), or ``pages_data[p]`` holds P*128 e4m3 bytes and
     ``pages_scale`` is unused (k_dtype "e4m3").
-    Returns (logits[r][h][t], blocks[r][h][j]) as nested lists of Python floats
-    holding fp32 values.
+    Returns (logits[r][h][t], blocks[r][h][j], mags[r][h][t]): logits and
+    blocks as nested lists of Python floats holding fp32 values, mags as exact
+    Fractions (0 for dead tokens; computed for the MXFP4 cache only).
     """
     B = len(seq_lens)
     if mode == "decode":
@@ -150,12 +174,13 @@ def score(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size
                 rows.append((b, min(seq_lens[b], prefix_lens[b] + i + 1)))
     nb = (max_seq_len + page_size - 1) // page_size
     s = Fraction(sm_scale)
-    logits, blocks = [], []
+    logits, blocks, mags = [], [], []
     for r, (b, limit) in enumerate(rows):
         limit = max(0, min(limit, max_seq_len))
         H = len(q_rows[r])
         lr = [[NEG_INF] * max_seq_len for _ in range(H)]
         br = [[NEG_INF] * nb for _ in range(H)]
+        mr = [[Fraction(0)] * max_seq_len for _ in range(H)]
         qh = [decode_q(q_rows[r][h], q_dtype) for h in range(H)]
         for t in range(limit):
             page = block_table[b][t // page_size]
@@ -170,9 +195,12 @@ def score(*, mode: str, q_rows, q_dtype: str, pages_data, pages_scale, page_size
                     dot = sum((qh[h][e] * kv[e] for e in range(128)), Fraction(0))
                     val = round_f32(s * dot)
                 lr[h][t] = val
+                if k_dtype != "e4m3" and not any(v is None for v in qh[h]):
+                    mr[h][t] = token_mag(qh[h], pages_data[page], pages_scale[page], t % page_size)
                 j = t // page_size
                 if val > br[h][j]:
                     br[h][j] = val
         logits.append(lr)
         blocks.append(br)
-    return logits, blocks
+        mags.append(mr)
+    return logits, blocks, mags

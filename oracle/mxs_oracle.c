@@ -243,6 +243,10 @@ static double q_hat(const mxo_args* a, int64_t row, int h, int e) {
 }
 
 int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
+  return mxo_score_ex(a, logits, blocks, mags, NULL);
+}
+
+int mxo_score_ex(const mxo_args* a, float* logits, float* blocks, double* mags, double* block_mags) {
   int T, R, H, P, NB, W, err = 0;
   int64_t ri;
   if (!a || !a->q || !a->k_data || !a->block_table || !a->seq_lens) return -1;
@@ -288,6 +292,9 @@ int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
     if (mags)
       for (h = 0; h < H; ++h)
         for (t = 0; t < W; ++t) mags[((int64_t)ri * H + h) * W + t] = 0.0;
+    if (block_mags)
+      for (h = 0; h < H; ++h)
+        for (t = 0; t < NB; ++t) block_mags[((int64_t)ri * H + h) * NB + t] = 0.0;
     qv = (double*)malloc(sizeof(double) * (size_t)H * 128);
     for (h = 0; h < H; ++h)
       for (e = 0; e < 128; ++e) qv[h * 128 + e] = q_hat(a, r, h, e);
@@ -322,6 +329,10 @@ int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
           logit = mxo_round_scaled_terms(S, ex, 4, 18, a->sm_scale);
           if (logits) logits[((int64_t)ri * H + h) * W + t] = logit;
           if (mags) mags[((int64_t)ri * H + h) * W + t] = mag;
+          if (block_mags) {
+            double* mp = &block_mags[((int64_t)ri * H + h) * NB + j];
+            if (mag > *mp) *mp = mag;
+          }
           if (blocks) {
             float* bp = &blocks[((int64_t)ri * H + h) * NB + j];
             if (logit > *bp) *bp = logit;
@@ -352,6 +363,10 @@ int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags) {
         logit = mxo_round_scaled_sum(S, sb, a->sm_scale);
         if (logits) logits[((int64_t)ri * H + h) * W + t] = logit;
         if (mags) mags[((int64_t)ri * H + h) * W + t] = mag;
+        if (block_mags) {
+          double* mp = &block_mags[((int64_t)ri * H + h) * NB + j];
+          if (mag > *mp) *mp = mag;
+        }
         if (blocks) {
           float* bp = &blocks[((int64_t)ri * H + h) * NB + j];
           if (logit > *bp) *bp = logit;

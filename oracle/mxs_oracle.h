@@ -86,6 +86,13 @@ typedef struct mxo_args {
  * -1 bad argument, -2 block-table entry of a live page out of range. */
 int mxo_score(const mxo_args* a, float* logits, float* blocks, double* mags);
 
+/* mxo_score plus block_mags [R, H, NB]: for each (row, head, page) the largest
+ * mags value among the page's live tokens (0 when the page has none). That is
+ * the M of a block score: a block score is the maximum of its page's logits,
+ * so an error of at most eps * M_t on every logit t moves it by at most
+ * eps * max_t M_t. Any output may be NULL. */
+int mxo_score_ex(const mxo_args* a, float* logits, float* blocks, double* mags, double* block_mags);
+
 /* Rows a selection would hold when rows == NULL. */
 int mxo_total_rows(const mxo_args* a);
 

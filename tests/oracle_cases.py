@@ -14,12 +14,16 @@ SM_SCALE = float(np.uint32(0x3DB504F3).view(np.float32))   # RN32(1/sqrt(128))
 
 
 def parse_assign(spec: str, n: int, width: int) -> List[int]:
-    """'all=X' or 'i=X j=Y ...' (hex values) -> list of n ints."""
+    """'all=X', 'i=X j=Y ...' or 'a-b=X' (hex values, index ranges inclusive) -> list of n ints."""
     out = [0] * n
     for tok in spec.split():
         k, v = tok.split("=")
         if k == "all":
             out = [int(v, 16)] * n
+        elif "-" in k:
+            lo, hi = (int(x) for x in k.split("-"))
+            for i in range(lo, hi + 1):
+                out[i] = int(v, 16)
         else:
             out[int(k)] = int(v, 16)
     for x in out:
@@ -34,9 +38,10 @@ def load_hand_pages() -> List[Dict]:
             line = line.strip()
             if not line or line.startswith("#"):
                 continue
-            name, q, data, scales, dot, bits = [x.strip() for x in line.split("|")]
+            name, q, data, scales, dot, bits, mag = [x.strip() for x in line.split("|")]
             cases.append(dict(name=name, q=parse_assign(q, 128, 16), data=parse_assign(data, 64, 8),
-                              scales=[int(x) for x in scales.split()], dot=float(dot), bits=int(bits, 16)))
+                              scales=[int(x) for x in scales.split()], dot=float(dot), bits=int(bits, 16),
+                              mag=float(mag)))
     return cases
 
 
@@ -62,18 +67,22 @@ def run_c(case, *, mode="prefill", q_dtype="bf16", page_size=128, max_seq_len=No
                         prefix_lens=case.get("prefix_lens"), want_mags=want_mags, **kw)
 
 
-def run_brute(case, *, mode="prefill", q_dtype="bf16", page_size=128, max_seq_len=None, sm_scale=SM_SCALE):
+def run_brute(case, *, mode="prefill", q_dtype="bf16", page_size=128, max_seq_len=None, sm_scale=SM_SCALE,
+              want_mags=False):
     ms = max_seq_len if max_seq_len is not None else int(np.max(case["seq_lens"])) if len(case["seq_lens"]) else 0
     q = case["q"]
     q_rows = [[list(map(int, q[r, h])) for h in range(q.shape[1])] for r in range(q.shape[0])]
     pages_data = [bytes(case["k_data"][p].reshape(-1)) for p in range(case["k_data"].shape[0])]
     pages_scale = [bytes(case["k_scale"][p].reshape(-1)) for p in range(case["k_scale"].shape[0])]
     bt = [list(map(int, row)) for row in case["block_table"]]
-    return brute.score(mode=mode, q_rows=q_rows, q_dtype=q_dtype, pages_data=pages_data, pages_scale=pages_scale,
-                       page_size=page_size, block_table=bt, seq_lens=list(map(int, case["seq_lens"])),
-                       max_seq_len=ms, sm_scale=sm_scale,
-                       cu_seqlens_q=None if case.get("cu_seqlens_q") is None else list(map(int, case["cu_seqlens_q"])),
-                       prefix_lens=None if case.get("prefix_lens") is None else list(map(int, case["prefix_lens"])))
+    kw = dict(mode=mode, q_rows=q_rows, q_dtype=q_dtype, pages_data=pages_data, pages_scale=pages_scale,
+              page_size=page_size, block_table=bt, seq_lens=list(map(int, case["seq_lens"])),
+              max_seq_len=ms, sm_scale=sm_scale,
+              cu_seqlens_q=None if case.get("cu_seqlens_q") is None else list(map(int, case["cu_seqlens_q"])),
+              prefix_lens=None if case.get("prefix_lens") is None else list(map(int, case["prefix_lens"])))
+    if want_mags:
+        return brute.score_mags(**kw)
+    return brute.score(**kw)
 
 
 def random_case(rng: np.random.Generator, *, B: int, H: int, page_size: int, q_lens, prefix_lens, seq_lens,

@@ -24,6 +24,14 @@ def _hand_pins_pass():
     return True
 
 
+def _hand_mag_pins_pass():
+    for case in load_hand_pages():
+        _, _, mb = run_brute(single_token_case(case["q"], case["data"], case["scales"]), want_mags=True)
+        if mb[0][0][0] != Fraction(case["mag"]):
+            return False
+    return True
+
+
 def _swapped_nibbles(data_page, scale_page, slot):
     out = []
     for e in range(128):
@@ -92,3 +100,29 @@ def test_planted_off_by_one_mask_is_caught(monkeypatch):
     monkeypatch.setattr(brute, "score", exclusive_diagonal)
     lb2, _ = run_brute(c, page_size=64, max_seq_len=4)
     assert [[np.isfinite(v) for v in row[0]] for row in lb2] != good
+
+
+# Planted mistakes in the twin's M (sum_e |Q_hat[e] K[e]|): each must fail the
+# hand-worked M of tests/golden/hand_pages.txt.
+_ORIG_MAG = brute.token_mag
+_SM = Fraction(float(np.uint32(0x3DB504F3).view(np.float32)))
+
+
+def _mag_without_e8m0(qh, data_page, scale_page, slot):
+    return _ORIG_MAG(qh, data_page, bytes([127]) * len(scale_page), slot)
+
+
+def _mag_with_sm_scale(qh, data_page, scale_page, slot):
+    return _ORIG_MAG(qh, data_page, scale_page, slot) * _SM
+
+
+def _mag_of_signed_sum(qh, data_page, scale_page, slot):
+    k = brute.token_k(data_page, scale_page, slot)
+    return abs(sum((qh[e] * k[e] for e in range(128)), Fraction(0)))
+
+
+@pytest.mark.parametrize("replacement", [_mag_without_e8m0, _mag_with_sm_scale, _mag_of_signed_sum])
+def test_planted_magnitude_mistake_is_caught(monkeypatch, replacement):
+    assert _hand_mag_pins_pass()
+    monkeypatch.setattr(brute, "token_mag", replacement)
+    assert not _hand_mag_pins_pass(), f"planted mistake {replacement.__name__} was not caught"

@@ -150,7 +150,7 @@ def test_hand_worked_pages(oracle_lib, case):
     # Values derived by hand (tests/golden/hand_pages.txt). Catches: nibble
     # order, scale-byte to block mapping, Q rounding, sign handling.
     c = single_token_case(case["q"], case["data"], case["scales"])
-    r = run_c(c, want_mags=True)
+    r = run_c(c, want_mags=True, want_block_mags=True)
     got = r.logits[0, 0, 0]
     assert f32_bits(got) == case["bits"], (case["name"], hex(f32_bits(got)))
     exact = Fraction(case["dot"]) * Fraction(SM_SCALE)
@@ -158,6 +158,75 @@ def test_hand_worked_pages(oracle_lib, case):
     assert r.blocks[0, 0, 0] == got
     lb, bb = run_brute(c)
     assert f32_bits(lb[0][0][0]) == case["bits"]
+
+
+@pytest.mark.parametrize("case", load_hand_pages(), ids=lambda c: c["name"])
+def test_hand_worked_magnitudes(oracle_lib, case):
+    # M = sum_e |Q_hat[e] * K[e]| worked by hand (last field of
+    # tests/golden/hand_pages.txt): the size of the terms a dot adds, which
+    # bounds the rounding error of any summation order and so sets how far a
+    # reordered (MFMA) sum may stray. The "alternating" and "crossblock" pages
+    # cancel to a zero dot with M = 128 and 528. Catches: the e8m0 factor
+    # dropped from M, sm_scale applied to M, |sum| instead of a sum of
+    # magnitudes, M of dead tokens, a block M that is not the page maximum.
+    c = single_token_case(case["q"], case["data"], case["scales"])
+    r = run_c(c, want_mags=True, want_block_mags=True)
+    assert r.mags[0, 0, 0] == case["mag"], (case["name"], r.mags[0, 0, 0])
+    assert r.block_mags[0, 0, 0] == case["mag"]
+    assert np.all(r.mags[0, 0, 1:] == 0.0)                          # no live token there
+    _, _, mb = run_brute(c, want_mags=True)
+    assert mb[0][0][0] == Fraction(case["mag"])
+    # |dot| <= M, with equality iff no two products have opposite signs
+    assert abs(case["dot"]) <= case["mag"]
+
+
+@pytest.mark.parametrize("seed,q_dtype", [(0, "bf16"), (1, "e4m3")])
+def test_magnitudes_match_fraction_twin_wide_bytes(oracle_lib, seed, q_dtype):
+    # C oracle's M (double) against the twin's exact Fraction M on random tiny
+    # batches with all 16 codes and e8m0 bytes 100..150 (a 2^50 spread of
+    # block scales: the four scaled block sums of the C oracle are added in
+    # double, so allow 2^-50 relative). Block M = the largest M among the
+    # page's live tokens; dead tokens and pages have M = 0.
+    rng = np.random.default_rng(300 + seed)
+    P = 64
+    c = random_case(rng, B=2, H=2, page_size=P, q_lens=[2, 1], prefix_lens=[64, 0], seq_lens=[66, 9],
+                    q_dtype=q_dtype, scale_lo=100, scale_hi=150)
+    W = 70
+    r = run_c(c, page_size=P, max_seq_len=W, q_dtype=q_dtype, want_mags=True, want_block_mags=True)
+    lb, _, mb = run_brute(c, page_size=P, max_seq_len=W, q_dtype=q_dtype, want_mags=True)
+    NB = (W + P - 1) // P
+    for row in range(r.mags.shape[0]):
+        for h in range(2):
+            for t in range(W):
+                ref = mb[row][h][t]
+                got = r.mags[row, h, t]
+                if ref == 0:
+                    assert got == 0.0
+                else:
+                    assert abs(Fraction(got) - ref) <= ref * Fraction(1, 2 ** 50), (row, h, t)
+                    assert np.isfinite(lb[row][h][t])
+            for j in range(NB):
+                seg = [mb[row][h][t] for t in range(j * P, min((j + 1) * P, W))]
+                assert abs(Fraction(r.block_mags[row, h, j]) - max(seg)) <= max(seg) * Fraction(1, 2 ** 50)
+
+
+def test_magnitude_scale_shift_and_bound(oracle_lib):
+    # +1 on every e8m0 byte doubles every M exactly (as it doubles every dot),
+    # and every finite logit satisfies |logit| <= sm_scale * M up to one fp32
+    # rounding (|dot| <= M). Catches: M taken without the e8m0 factors (it
+    # would not double), M scaled by sm_scale (the bound would fail).
+    rng = np.random.default_rng(17)
+    c = random_case(rng, B=2, H=3, page_size=128, q_lens=[3, 2], prefix_lens=[129, 7], seq_lens=[132, 9],
+                    scale_lo=110, scale_hi=140, garbage_tail=False)
+    r0 = run_c(c, want_mags=True)
+    r1 = run_c(dict(c, k_scale=c["k_scale"] + 1), want_mags=True)
+    assert np.array_equal(r1.mags, 2.0 * r0.mags)
+    fin = np.isfinite(r0.logits)
+    lg = r0.logits[fin].astype(np.float64)
+    m = r0.mags[fin]
+    assert np.all(np.abs(lg) <= SM_SCALE * m * (1 + 2.0 ** -23))
+    assert np.all(m[np.abs(lg) > 0] > 0)
+    assert np.all(r0.mags[~fin] == 0.0)
 
 
 def test_causal_prefix_example(oracle_lib):
