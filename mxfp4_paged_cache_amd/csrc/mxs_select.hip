@@ -28,9 +28,12 @@ using namespace dev;
 //   * every candidate but the tail lies in [x, K] (K the largest non-tail
 //     key), so T shares the leading bits x and K have in common and only the
 //     bits below them are searched.
+// Negative scores map to 0 - bits, which sends -0.0 to the key of +0.0 (the
+// two compare equal, so they tie and the lower page wins) and keeps every
+// other negative below it in order; a live key is never 0.
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t b = __float_as_uint(s);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (b & 0x80000000u) ? 0u - b : (b | 0x80000000u);
 }
 
 __device__ __forceinline__ uint32_t ballot_count(bool p) { return __builtin_popcountll(__ballot(p)); }
@@ -60,8 +63,14 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) { return wave_reduce<fa
 
 // The scores of one (row, head), all loads issued together (indices past NB
 // read the last page's score and are then dropped, so no load is predicated).
+// An empty window (NB = 0) reads nothing: every page is then dead.
 template <int PER>
 __device__ __forceinline__ void load_scores(const SArgs& a, int64_t r, int h, int lane, float (&v)[PER]) {
+  if (a.NB <= 0) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) v[m] = -__builtin_inff();
+    return;
+  }
   const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
 #pragma unroll
   for (int m = 0; m < PER; ++m) v[m] = srow[min(64 * m + lane, a.NB - 1)];

@@ -137,3 +137,43 @@ def test_full_size_selection_sampled_rows():
     # every selection holds its row's tail page
     tails = (torch.from_numpy(lim).cuda() - 1) // wl.page_size
     assert bool((got == tails[:, None, None]).any(dim=2).all())
+
+
+def test_signed_zeros_tie_at_the_kth_place():
+    # -0.0 and +0.0 compare equal, so they tie and the lower page wins: with
+    # the k-th place contested by zeros of both signs, the lowest-indexed
+    # zeros are taken whatever their sign (oracle/topk.py sorts by value, then
+    # by page index)
+    P, NB, H = 64, 200, 4
+    rng = np.random.default_rng(5)
+    R = 3
+    s = np.full((R, H, NB), -1.0, np.float32)
+    for r in range(R):
+        for h in range(H):
+            s[r, h, rng.choice(NB, 6, replace=False)] = 2.0          # 6 clear winners
+            z = rng.choice(NB, 12, replace=False)
+            s[r, h, z] = np.where(rng.random(12) < 0.5, np.float32(-0.0), np.float32(0.0))
+    seq = [NB * P] * R
+    lim = topk.row_limits("decode", seq, NB * P)
+    for k in (8, 10, 13):
+        ref = topk.select_pages(s, lim, P, k)
+        got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"),
+                              NB * P, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), ref), k
+    say("  signed zeros at the k-th place: selections equal the oracle's")
+
+
+def test_empty_window_reads_nothing_and_pads():
+    # max_seq_len 0: no page is live, every row is k entries of -1, and no
+    # score is read (the scores tensor has one column and starts its own
+    # allocation; a read before it would land outside)
+    R, H, k = 5, 3, 4
+    bs = torch.full((R, H, 1), float("nan"), device="cuda")
+    seq = torch.zeros(R, dtype=torch.int32, device="cuda")
+    got = mx.select_pages(bs, k, seq, 0, 64)
+    cu = torch.tensor([0, 2, 5], dtype=torch.int32, device="cuda")
+    got_p = mx.select_pages(bs, k, torch.zeros(2, dtype=torch.int32, device="cuda"), 0, 128, cu_seqlens_q=cu,
+                            prefix_lens=torch.zeros(2, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert (got == -1).all() and (got_p == -1).all()
