@@ -26,23 +26,26 @@ using namespace dev;
 // keeps all chunks of a request on one XCD, whose L2 then serves the
 // request's query and block-table row to every chunk.
 // ---------------------------------------------------------------------------
-// One page in registers. load(): dp/sp are the page's (uniform) bases,
-// doff/soff the lane's byte offsets inside the page (MXFP4: data 64 i + 16 g,
-// scale 4 i + g; fp8: 16 * lane).
+// One page in registers. load(): dr/sr are buffer resources over the page's
+// data and scale bytes (uniform; empty for a refill past the chunk's last
+// live page, whose loads then return zeros and move no bytes), doff/soff the
+// lane's byte offsets inside the page (MXFP4: data 64 i + 16 g, scale
+// 4 i + g; fp8: 16 * lane).
 template <int KDT, int P>
 struct RegPage;
 
 template <int P>
 struct RegPage<MXS_K_MXFP4, P> {
+  static constexpr uint32_t kDataBytes = P * 64, kScaleBytes = P * 4;
   u4 d[P / 16];
   int s[P / 16];
   static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(i * 64 + 16 * g); }
   __device__ __forceinline__ KTile<MXS_K_MXFP4> tile(int t) const { return {d[t], s[t]}; }
-  __device__ __forceinline__ void load(const uint8_t* dp, const uint8_t* sp, uint32_t doff, uint32_t soff) {
+  __device__ __forceinline__ void load(rsrc_t dr, rsrc_t sr, uint32_t doff, uint32_t soff) {
 #pragma unroll
     for (int t = 0; t < P / 16; ++t) {
-      d[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 1024u * t));
-      s[t] = __builtin_nontemporal_load(sp + soff + 64u * t);
+      d[t] = buffer_load16_nt(dr, doff + 1024u * t);
+      s[t] = buffer_load1_nt(sr, soff + 64u * t);
     }
   }
 };
@@ -55,14 +58,15 @@ struct RegPage<MXS_K_MXFP4, P> {
 // (16 pieces of 64 bytes per instruction) measured about 20% slower.
 template <int P>
 struct RegPage<MXS_K_E4M3, P> {
+  static constexpr uint32_t kDataBytes = P * 128, kScaleBytes = 0;
   u4 c0[P / 16];   // chunk `lane` of tile t
   u4 c1[P / 16];   // chunk 64 + `lane` of tile t
   static __device__ __forceinline__ uint32_t data_offset(int g, int i) { return (uint32_t)(16 * (16 * g + i)); }
-  __device__ __forceinline__ void load(const uint8_t* dp, const uint8_t*, uint32_t doff, uint32_t) {
+  __device__ __forceinline__ void load(rsrc_t dr, rsrc_t, uint32_t doff, uint32_t) {
 #pragma unroll
     for (int t = 0; t < P / 16; ++t) {
-      c0[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t));
-      c1[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(dp + doff + 2048u * t + 1024u));
+      c0[t] = buffer_load16_nt(dr, doff + 2048u * t);
+      c1[t] = buffer_load16_nt(dr, doff + 2048u * t + 1024u);
     }
   }
   // tiles [HF * P / 32, (HF + 1) * P / 32) into buf (P * 64 bytes) as tiles 0.. of the fp8 layout
@@ -193,11 +197,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   if (j0 < jl) {
     const uint32_t doff = RegPage<KDT, P>::data_offset(g, i);
     const uint32_t soff = (uint32_t)(i * 4 + g);
+    // Refills past the chunk's last live page (the pipeline's tail) go
+    // through empty buffer resources: they issue and retire like real loads,
+    // so every wait stays exact, but fetch nothing (with the last live page
+    // re-read instead, 34 page loads per 32-page chunk reached HBM).
     auto load_page = [&](RegPage<KDT, P>& kp, int j) {
-      const int jj = min(j, jl - 1);
-      const int64_t page = __builtin_amdgcn_readlane(my_page, jj - j0);
-      kp.load(a.kd + page * a.kd_page_stride, KDT == MXS_K_MXFP4 ? a.ks + page * a.ks_page_stride : nullptr, doff,
-              soff);
+      const bool live = j < jl;
+      const int64_t page = __builtin_amdgcn_readlane(my_page, min(j, jl - 1) - j0);
+      const rsrc_t dr = buffer_rsrc(a.kd + page * a.kd_page_stride, live ? RegPage<KDT, P>::kDataBytes : 0u);
+      const rsrc_t sr = KDT == MXS_K_MXFP4
+                            ? buffer_rsrc(a.ks + page * a.ks_page_stride, live ? RegPage<KDT, P>::kScaleBytes : 0u)
+                            : dr;
+      kp.load(dr, sr, doff, soff);
     };
     auto score = [&](const RegPage<KDT, P>& kp, int j) {
       const int lip = limit - j * P;                 // live tokens in this page

@@ -263,5 +263,21 @@ __device__ __forceinline__ void stage_store(const PageStage<KDT, P>& st, uint8_t
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Raw buffer resource over [base, base + bytes) (no stride, no swizzle).
+// A buffer load at an offset at or past `bytes` returns zeros without a
+// memory request, so bytes = 0 turns every load through the resource into a
+// no-op that still issues and retires like any other load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;   // cache-policy operand of a buffer load: nt (streamed once)
+__device__ __forceinline__ u4 buffer_load16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+}
+__device__ __forceinline__ int buffer_load1_nt(rsrc_t r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, kNonTemporal);
+}
+
 }  // namespace dev
 }  // namespace mxs
