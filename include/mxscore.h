@@ -175,6 +175,9 @@ typedef struct mxs_plan {
   int64_t items;               /* total work items */
   int32_t kernel;              /* internal kernel id */
   int32_t k_dtype;             /* cache dtype the plan was made for */
+  int32_t xcd_split;           /* logits kernel: 1 = each of the 8 XCDs takes a contiguous eighth of the
+                                  work items (query slots split across XCDs), 0 = workgroups stride over all
+                                  items (page chunks split across XCDs); 0 for the other kernels */
 } mxs_plan;
 
 /* Compute a plan. parallel_unit_num > 0 overrides the workgroup count

@@ -88,7 +88,8 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "q_dtype", "page_size", "num_heads", "batch", "max_query_len", "max_seq_len", "want_logits",
         "want_blocks", "grid", "block", "slots_per_item", "pages_per_item", "slot_items", "page_items",
-        "head_groups")] + [("items", ctypes.c_int64), ("kernel", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
+        "head_groups")] + [("items", ctypes.c_int64), ("kernel", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
+                           ("xcd_split", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

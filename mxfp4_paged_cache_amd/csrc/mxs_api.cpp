@@ -540,13 +540,21 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t pa
         }
       }
     } else {
-      // Logits are written page chunk fastest. Chunk counts in multiples of 8
-      // (when there are pages enough): with a grid that is also a multiple of
-      // 8, workgroup c only sees chunks c mod 8, so each of the 8 XCDs reads
-      // one eighth of the pages into its own L2.
+      // Logits are written page chunk fastest, and each XCD's L2 should hold
+      // only the part of the inputs its workgroups need. When the query slots
+      // outweigh the pages they are scored against (a request's query bytes
+      // above its cache bytes), the items are split across the 8 XCDs in
+      // contiguous eighths (xcd_split): an XCD then reads its eighth of the
+      // queries and the pages of its requests. Otherwise chunk counts go in
+      // multiples of 8 (when there are pages enough): with a grid that is
+      // also a multiple of 8, workgroup c only sees chunks c mod 8, so each
+      // XCD reads one eighth of the pages.
+      const int64_t q_bytes = (int64_t)p.max_query_len * num_heads * 128 * (q_dtype == MXS_Q_BF16 ? 2 : 1);
+      const int64_t k_bytes = NB * page_size * (k_dtype == MXS_K_E4M3 ? 128 : 68);
       const int64_t want_items = parallel_unit_num > 0 ? (int64_t)parallel_unit_num * 4 : capacity * 4;
       int64_t chunks = base > 0 ? ceil_div(want_items, base) : 1;
-      if (NB >= 8) chunks = ceil_div(chunks, 8) * 8;
+      p.xcd_split = q_bytes > k_bytes && grid % 8 == 0 ? 1 : 0;
+      if (NB >= 8 && !p.xcd_split) chunks = ceil_div(chunks, 8) * 8;
       if (chunks > NB) chunks = NB;
       if (chunks < 1) chunks = 1;
       ppi = ppi_for(chunks);
@@ -556,6 +564,12 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t pa
     p.items = base * p.page_items;
     if (grid > p.items) grid = p.items;
     if (grid < 1) grid = 1;
+    if (p.xcd_split) {   // eight equal groups of workgroups, one per XCD
+      if (grid >= 8)
+        grid = grid / 8 * 8;
+      else
+        p.xcd_split = 0;
+    }
     p.grid = (int32_t)grid;
   }
   if (p.items > INT32_MAX * (int64_t)mxs::kWaves || p.grid > INT32_MAX) return fail(MXS_EINVAL, "problem too large");
@@ -610,13 +624,14 @@ bool plan_consistent(const mxs_plan& p, int mode, int32_t H, int32_t B, int32_t 
   if (p.block != mxs::kThreads || p.grid < 1 || p.pages_per_item < 1 || p.page_items < 1) return false;
   if ((int64_t)p.page_items * p.pages_per_item < NB) return false;
   if (mode == MXS_MODE_DECODE && !p.want_logits) {
-    return p.kernel == mxs::KID_DECODE && p.head_groups == ceil_div(H, mxs::kDecodeHeads) &&
+    return p.kernel == mxs::KID_DECODE && p.xcd_split == 0 && p.head_groups == ceil_div(H, mxs::kDecodeHeads) &&
            p.pages_per_item <= mxs::kDecodeMaxPages && p.page_items % mxs::kWaves == 0 &&
            p.items == (int64_t)B * p.head_groups * p.page_items && (int64_t)p.grid * mxs::kWaves == p.items;
   }
   const bool lgk = mode == MXS_MODE_LOGITS || p.want_logits;
   const int32_t kid = lgk ? mxs::KID_LOGITS : mxs::KID_PREFILL;
   const int64_t slots = (int64_t)max_query_len * H;
+  if (p.xcd_split != 0 && (p.xcd_split != 1 || !lgk || p.grid % 8 != 0)) return false;
   return p.kernel == kid && p.slots_per_item == (lgk ? mxs::kLogitsSlotsPerItem : mxs::kPrefillSlotsPerItem) &&
          p.slot_items == (slots > 0 ? ceil_div(slots, p.slots_per_item) : 0) &&
          p.items == (int64_t)B * p.slot_items * p.page_items && p.grid <= (p.items > 0 ? p.items : 1);
@@ -747,6 +762,7 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   a.head_groups = plan.head_groups;
   a.items = plan.items;
   a.decode_rows = decode && plan.kernel == mxs::KID_LOGITS ? 1 : 0;
+  a.xcd_split = plan.xcd_split;
   hipError_t e = mxs::launch(plan, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MXS_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   return MXS_OK;

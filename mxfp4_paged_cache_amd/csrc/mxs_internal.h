@@ -65,6 +65,7 @@ struct KArgs {
   int32_t vec_bs;           // widest vector store the block-score rows allow, in floats (4, 2 or 1)
   int32_t vec_lg;           // logit rows 16-byte aligned
   int32_t decode_rows;      // logits kernel: row b is request b (one query row, limit = seq_len[b])
+  int32_t xcd_split;        // logits kernel: XCD x takes items [x * items / 8, (x + 1) * items / 8)
 };
 
 // Arguments of the page-selection kernel (mxs_select.hip).

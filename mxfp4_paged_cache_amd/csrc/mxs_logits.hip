@@ -21,10 +21,13 @@ using namespace dev;
 // layout, each instruction would write 64-byte pieces of 16 different rows,
 // which measured at about half the write bandwidth on this chip.
 //
-// Work items are ordered page chunk fastest; with a grid and a chunk count
-// that are both multiples of 8, workgroup c only sees chunks c mod 8
-// (workgroups go round-robin over the 8 XCDs), so each XCD keeps one eighth
-// of the pages in its own L2.
+// Work items are ordered page chunk fastest. Workgroups go round-robin over
+// the 8 XCDs, so with a grid and a chunk count that are both multiples of 8,
+// workgroup c only sees chunks c mod 8 and each XCD keeps one eighth of the
+// pages in its own L2. When the queries outweigh the pages (xcd_split), XCD
+// x instead takes the contiguous items [x items / 8, (x + 1) items / 8),
+// strided over its own workgroups: its eighth of the query slots and the
+// pages they are scored against.
 // ---------------------------------------------------------------------------
 constexpr int kLogitsSlots = kWaves * 16;   // query slots per work item
 constexpr int kWinTokens = 128;             // tokens per output window: 512 bytes of a logits row
@@ -47,7 +50,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
   // write-out map: lanes 0..31 write row 2q, lanes 32..63 row 2q + 1, 16 bytes each
   const int wrow = lane >> 5, wcol = lane & 31;
 
-  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+  int64_t item_lo = 0, item_hi = a.items, item0 = blockIdx.x, item_step = gridDim.x;
+  if (a.xcd_split) {   // the plan makes the grid a multiple of 8
+    const int x = blockIdx.x & 7;
+    item_lo = a.items * x / 8;
+    item_hi = a.items * (x + 1) / 8;
+    item0 = item_lo + (blockIdx.x >> 3);
+    item_step = gridDim.x >> 3;
+  }
+  for (int64_t item = item0; item < item_hi; item += item_step) {
     const int pc = (int)(item % a.page_items);
     const int64_t rest = item / a.page_items;
     const int sb = (int)(rest % a.slot_items);
