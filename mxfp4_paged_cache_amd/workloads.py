@@ -10,7 +10,9 @@ Recipe (the pages' scorer benchmarks use random K data with e8m0 bytes in
   workload hands the query over as e4m3;
 * K data: uniform random bytes, so both e2m1 codes of a byte are uniform over
   all 16 codes;
-* K scales: uniform random e8m0 bytes in [lo, hi] per (token, 32-element block);
+* K scales: uniform random e8m0 bytes in [lo, hi], one per (token, 32-element
+  block), or one per token repeated over its four blocks (scale_mode "token",
+  the chunked-prefill workload's per-token bytes);
 * fp8 cache (k_dtype "e4m3", the format the MXFP4 one replaces): 128 bytes
   per token drawn uniformly over the 254 finite e4m3 codes, no scale view;
 * block table: distinct pages drawn without replacement from a larger pool, so
@@ -49,6 +51,7 @@ class Workload:
     q_dtype: str = "bf16"           # "bf16" | "e4m3"
     scale_lo: int = 122
     scale_hi: int = 127
+    scale_mode: str = "block"       # "block": a byte per (token, 32-block); "token": one byte per token
     pool_pages: int = 0             # 0 -> exactly the pages the requests need
     want_logits: bool = False
     want_blocks: bool = True
@@ -157,6 +160,15 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
     tb = 128 if fp8 else SLOT_DATA_BYTES     # data bytes per token
     sb = 0 if fp8 else SLOT_SCALE_BYTES      # scale bytes per token
 
+    def scale_bytes(shape):
+        # shape [..., 4]: one draw per block, or one per token repeated over its 4 blocks
+        if wl.scale_mode == "token":
+            one = torch.randint(wl.scale_lo, wl.scale_hi + 1, tuple(shape[:-1]) + (1,), generator=gs, device=device,
+                                dtype=torch.uint8)
+            return one.expand(*shape).contiguous()
+        return torch.randint(wl.scale_lo, wl.scale_hi + 1, tuple(shape), generator=gs, device=device,
+                             dtype=torch.uint8)
+
     def data_bytes(shape):
         if not fp8:
             return torch.randint(0, 256, shape, generator=gd, device=device, dtype=torch.uint8)
@@ -174,8 +186,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
                                 device=device, dtype=torch.uint8)
     elif wl.layout == "split":
         k_data = data_bytes((pool, P, tb))
-        k_scale = None if fp8 else torch.randint(wl.scale_lo, wl.scale_hi + 1, (pool, P, SLOT_SCALE_BYTES),
-                                                 generator=gs, device=device, dtype=torch.uint8)
+        k_scale = None if fp8 else scale_bytes((pool, P, SLOT_SCALE_BYTES))
     else:
         # One uint8 region. "region": page = [P x 64 B data][P x 4 B scale].
         # "shared": page block = two layer slots of that shape; slot 1 is scored,
@@ -192,8 +203,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
         k_data = torch.as_strided(region, (pool, P, tb), (stride, tb, 1), off)
         k_scale = None
         if not fp8:
-            scale_part = torch.randint(wl.scale_lo, wl.scale_hi + 1, (nused, P * SLOT_SCALE_BYTES), generator=gs,
-                                       device=device, dtype=torch.uint8)
+            scale_part = scale_bytes((nused, P, SLOT_SCALE_BYTES)).reshape(nused, P * SLOT_SCALE_BYTES)
             view[lo:hi, off + P * tb:off + slot] = scale_part
             k_scale = torch.as_strided(region, (pool, P, SLOT_SCALE_BYTES), (stride, SLOT_SCALE_BYTES, 1),
                                        off + P * tb)
@@ -254,9 +264,18 @@ def prefill_long() -> Workload:
 
 
 def prefill_chunk() -> Workload:
-    """32768-row chunk after a 100000-token prefix (context 132768), e8m0 bytes uniform in 100..150."""
+    """32768-row chunk after a 100000-token prefix (context 132768), one e8m0 byte per token, uniform in 100..150."""
     return Workload("prefill_chunk32k_ctx132768", "prefill", H=64, page_size=128, q_lens=[32768],
-                    prefix_lens=[100000], seq_lens=[132768], scale_lo=100, scale_hi=150, pool_pages=300_000)
+                    prefix_lens=[100000], seq_lens=[132768], scale_lo=100, scale_hi=150, scale_mode="token",
+                    pool_pages=300_000)
+
+
+def prefill_chunk_block_scales() -> Workload:
+    """The chunked prefill with an e8m0 byte drawn per (token, 32-element block) instead of per token."""
+    wl = prefill_chunk()
+    wl.name = "prefill_chunk32k_ctx132768_blockscales"
+    wl.scale_mode = "block"
+    return wl
 
 
 def logits_shared_pool() -> Workload:
@@ -324,4 +343,5 @@ CONFIGS = {
     9: prefill_long_fp8,
     10: write_1m_tokens_fp8,
     11: attn_decode_sparse,
+    12: prefill_chunk_block_scales,
 }
