@@ -1,26 +1,31 @@
 """Helpers shared by the GPU parity tests: run the HIP path, run the CPU
 oracle on the same seeded inputs, and compare under the documented rule.
 
-Comparison rule (per finite element):
-    |gpu - ref| <= max(2^-20 * |ref|, 2^-10 * sm_scale * M)
-where ref is the oracle's RN_fp32(sm_scale * exact dot) and M is the sum of
-|Q_hat[e] * K[e]| over the 128 elements (for a block score: the largest M
-among the page's live tokens). The first term is the relative bound asked
-for; the second is the measured error of the block-scaled MFMA under
-cancellation (groups of 8 elements keep about 12 bits below their largest
-product; worst measured 2^-11.95 * M), with a 4x margin. -inf positions,
-output indexing and the argmax over pages must match exactly (the argmax
-may differ only between values that are equal within the same bound).
-A floor on the fraction of bit-identical values guards against systematic
-drift that the per-element bound would let through.
+Comparison rule:
+* -inf positions (masking), output indexing and the argmax over pages
+  (lowest index on ties) are compared exactly;
+* every finite score should satisfy |gpu - ref| <= 2^-20 * |ref|, where ref is
+  the oracle's RN_fp32(sm_scale * exact dot) (a zero ref needs a zero gpu).
+The block-scaled MFMA is not an exactly rounded dot: within each group of 8
+adjacent elements it keeps about 12 bits below the group's largest product
+(measured on gfx950), so a dot whose terms cancel can miss the relative bound
+while its absolute error stays below 2^-11.95 * M (M = sum_e |Q_hat[e] K[e]|;
+for a block score, the largest M among the page's live tokens). Each case
+therefore states a ceiling on the number of finite values outside 2^-20
+relative and on the number of argmax positions that differ; every value
+outside must still be within 2^-10 * sm_scale * M (the measured bound with a
+4x margin), every differing argmax must be a near tie under that bound, and
+the counts are printed. The outputs are deterministic (one MFMA per logit,
+no atomics), so the counts are properties of the seeded inputs.
+A floor on the bit-identical fraction guards against systematic drift.
 
 An fp8 (e4m3) cache runs the same instruction with both operands e4m3. Its
 products carry 8 significant bits and, with K spread over all e4m3 codes,
 span about 2^17 within a group, so the group truncation shows on most values
 (measured on gfx950: 0.05% bit-identical for uniform codes, 23% for e4m3 of
 N(0, 1); err / (sm_scale * M) at most 2^-13.1, 99th percentile 2^-14.6).
-The per-element bound is unchanged; in place of the bit-identical floor the
-99th percentile of err / (sm_scale * M) must stay below 2^-12.
+Its tests bound the 99th percentile of err / (sm_scale * M) by 2^-12 in place
+of the bit-identical floor.
 """
 from __future__ import annotations
 
@@ -53,7 +58,8 @@ def q_numpy(q: torch.Tensor):
 
 
 def oracle_run(inp: W.Inputs, *, rows=None, want_logits=True, want_blocks=True, table: int = 0,
-               max_seq_len: Optional[int] = None, sm_scale: float = W.INV_SQRT_D, compact: bool = False):
+               max_seq_len: Optional[int] = None, sm_scale: float = W.INV_SQRT_D, compact: bool = False,
+               want_mags: bool = True, want_block_mags: bool = True):
     """Oracle on host copies of the inputs. ``compact`` gathers only the pages the
     block table references (valid because page order is irrelevant, a pinned property)."""
     wl = inp.wl
@@ -88,14 +94,8 @@ def oracle_run(inp: W.Inputs, *, rows=None, want_logits=True, want_blocks=True, 
                         block_table=bt, seq_lens=inp.seq_lens.cpu().numpy(),
                         max_seq_len=max_seq_len if max_seq_len is not None else wl.window, sm_scale=sm_scale,
                         cu_seqlens_q=inp.cu_seqlens_q.cpu().numpy(), prefix_lens=inp.prefix_lens.cpu().numpy(),
-                        rows=rows, want_logits=want_logits, want_blocks=want_blocks, want_mags=True)
-
-
-def block_mags(mags: np.ndarray, P: int, NB: int) -> np.ndarray:
-    R, H, Wd = mags.shape
-    pad = NB * P - Wd
-    m = np.concatenate([mags, np.zeros((R, H, pad))], axis=2) if pad > 0 else mags[:, :, :NB * P]
-    return m.reshape(R, H, NB, P).max(axis=3)
+                        rows=rows, want_logits=want_logits, want_blocks=want_blocks,
+                        want_mags=want_mags and want_logits, want_block_mags=want_block_mags and want_blocks)
 
 
 @dataclass
@@ -103,12 +103,16 @@ class Stats:
     n: int
     finite: int
     exact: float
-    within_rel: float
+    outside: int          # finite values outside 2^-20 relative
     max_rel: float
 
 
 def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, *, what: str,
-            min_exact: float, p99_max: Optional[float] = None) -> Stats:
+            max_outside, min_exact: float = 0.0, p99_max: Optional[float] = None) -> Stats:
+    """Element-by-element comparison (rule above). ``max_outside``: the case's
+    ceiling on finite values outside 2^-20 relative, a count (int) or, for the
+    fp8 cache where most values are outside, a fraction of the finite values
+    (float)."""
     gpu = np.asarray(gpu, np.float32)
     ref = np.asarray(ref, np.float32)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
@@ -121,18 +125,23 @@ def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, 
     r = ref[fin].astype(np.float64)
     m = mag[fin]
     err = np.abs(g - r)
-    tol = np.maximum(REL * np.abs(r), ABS_M * sm_scale * m)
-    bad = err > tol
-    if bad.any():
-        k = np.argmax(err - tol)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {len(r)} values outside the bound; worst gpu={g[k]!r} "
-                             f"ref={r[k]!r} M={m[k]!r} tol={tol[k]!r}")
-    same = (g == r)
-    exact = float(same.mean()) if len(r) else 1.0
-    within = float((err <= REL * np.abs(r)).mean()) if len(r) else 1.0
+    out = err > REL * np.abs(r)
+    n_out = int(out.sum())
+    exact = float((g == r).mean()) if len(r) else 1.0
     max_rel = float(np.max(err / np.maximum(np.abs(r), 1e-300))) if len(r) else 0.0
-    st = Stats(gpu.size, int(fin.sum()), exact, within, max_rel)
-    say(f"  {what}: {st.finite}/{st.n} finite, bit-exact {exact:.6f}, within 2^-20 rel {within:.6f}, max rel {max_rel:.3g}")
+    st = Stats(gpu.size, int(fin.sum()), exact, n_out, max_rel)
+    ceiling = max_outside if isinstance(max_outside, int) else int(np.floor(max_outside * st.finite))
+    say(f"  {what}: {st.finite}/{st.n} finite, bit-exact {exact:.6f}, outside 2^-20 rel {n_out} "
+        f"({n_out / max(st.finite, 1):.3g}; ceiling {ceiling}), max rel {max_rel:.3g}")
+    if n_out:
+        bound = ABS_M * sm_scale * m[out]
+        k = int(np.argmax(err[out] / np.maximum(bound, 1e-300)))
+        say(f"  {what}: worst outside: gpu={g[out][k]!r} ref={r[out][k]!r} M={m[out][k]!r} "
+            f"err/(sm_scale*M)={err[out][k] / max(sm_scale * m[out][k], 1e-300):.3g}")
+        bad = err[out] > bound
+        assert not bad.any(), (f"{what}: {int(bad.sum())} values outside 2^-20 relative are also outside "
+                               f"2^-10 * sm_scale * M: gpu={g[out][bad][:3]} ref={r[out][bad][:3]} M={m[out][bad][:3]}")
+    assert n_out <= ceiling, f"{what}: {n_out} values outside 2^-20 relative, ceiling {ceiling}"
     assert exact >= min_exact, f"{what}: bit-exact fraction {exact:.6f} below floor {min_exact}"
     if p99_max is not None and len(r):
         rel_m = err / np.maximum(sm_scale * m, 1e-300)
@@ -142,23 +151,29 @@ def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, 
     return st
 
 
-def compare_argmax(gpu_bs: np.ndarray, ref_bs: np.ndarray, mag_b: np.ndarray, sm_scale: float, what: str):
-    """Argmax over pages (lowest index on ties, -1 when all -inf) must match,
-    unless the two candidates are equal within the comparison bound."""
-    def amax(x):
-        a = np.argmax(x, axis=-1)
-        allinf = np.all(np.isneginf(x), axis=-1)
-        return np.where(allinf, -1, a)
-    ag, ar = amax(gpu_bs), amax(ref_bs)
+def argmax_pages(x: np.ndarray) -> np.ndarray:
+    """Argmax over the last axis, lowest index on ties, -1 where every value is -inf."""
+    a = np.argmax(x, axis=-1)
+    return np.where(np.all(np.isneginf(x), axis=-1), -1, a)
+
+
+def compare_argmax(gpu_bs: np.ndarray, ref_bs: np.ndarray, mag_b: np.ndarray, sm_scale: float, what: str,
+                   max_diff: int = 0) -> int:
+    """Argmax over pages must match; a case states a ceiling (normally 0) on
+    positions that differ, and each of those must be a near tie: the oracle's
+    values at the two pages differ by at most twice the MFMA bound."""
+    ag, ar = argmax_pages(gpu_bs), argmax_pages(ref_bs)
     diff = np.argwhere(ag != ar)
     for idx in diff:
         idx = tuple(idx)
         jg, jr = ag[idx], ar[idx]
         assert jg >= 0 and jr >= 0, f"{what}: argmax differs on an all -inf row"
         vg, vr = float(ref_bs[idx + (jg,)]), float(ref_bs[idx + (jr,)])
-        tol = max(REL * abs(vr), ABS_M * sm_scale * max(mag_b[idx + (jg,)], mag_b[idx + (jr,)])) * 2
+        tol = ABS_M * sm_scale * max(mag_b[idx + (jg,)], mag_b[idx + (jr,)]) * 2
         assert abs(vg - vr) <= tol, f"{what}: argmax {jg} vs {jr} at {idx} is not a near tie ({vg} vs {vr})"
-    say(f"  {what}: argmax over pages equal on {ag.size - len(diff)}/{ag.size} (rest near ties)")
+    say(f"  {what}: argmax over pages differs on {len(diff)}/{ag.size} (ceiling {max_diff})")
+    assert len(diff) <= max_diff, f"{what}: argmax differs on {len(diff)} rows, ceiling {max_diff}"
+    return len(diff)
 
 
 def gpu_inputs(inp: W.Inputs) -> W.Inputs:

@@ -13,15 +13,18 @@ import oracle
 import mxfp4_paged_cache_amd as mx
 from mxfp4_paged_cache_amd import workloads as W
 from oracle import writer
-from tests.gpu_helpers import (block_mags, compare, compare_argmax, gpu_inputs, oracle_run, run_gpu, say)
+from tests.gpu_helpers import (compare, compare_argmax, gpu_inputs, oracle_run, run_gpu, say)
 from tests.test_gpu_write import make_keys
+from tests.test_gpu_parity import _sample_rows
 
 pytestmark = pytest.mark.gpu
 
 S = W.INV_SQRT_D
 # e4m3 x e4m3 products are not summed exactly by the MFMA (see tests/gpu_helpers.py):
-# the per-element bound holds, and the error distribution replaces the bit-exact floor
-FP8 = dict(min_exact=0.0, p99_max=2.0 ** -12)
+# 91-99% of the values miss 2^-20 relative (measured; the ceiling is a fraction of
+# the finite values), every value is within 2^-10 * sm_scale * M, and the error
+# distribution replaces the bit-exact floor
+FP8 = dict(min_exact=0.0, p99_max=2.0 ** -12, max_outside=0.995)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,7 +56,7 @@ def check_case(wl: W.Workload, *, seed=0):
     bs, lg = run_gpu(dev)
     torch.cuda.synchronize()
     ref = oracle_run(host, want_logits=True, want_blocks=True)
-    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    mb = ref.block_mags
     if bs is not None:
         compare(bs.cpu().numpy(), ref.blocks, mb, S, what="block scores", **FP8)
         compare_argmax(bs.cpu().numpy(), ref.blocks, mb, S, "block scores")
@@ -151,11 +154,12 @@ def test_fp8_equals_mxfp4_inside_window(mode):
     # over [119, 133] put the four block sums up to 2^14 apart, where the
     # MFMA's sum is not always the rounded exact one (as for the MXFP4 path's
     # wide-scale cases): the bound holds, the bit-identical floor is theirs.
-    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    mb = ref.block_mags
     if bs8 is not None:
-        compare(bs8.cpu().numpy(), ref.blocks, mb, S, what="fp8 block scores", min_exact=0.60)
+        compare(bs8.cpu().numpy(), ref.blocks, mb, S, what="fp8 block scores", min_exact=0.60, max_outside=0)
     if lg8 is not None:
-        compare(lg8.cpu().numpy(), ref.logits, ref.mags, S, what="fp8 logits", min_exact=0.60)
+        compare(lg8.cpu().numpy(), ref.logits, ref.mags, S, what="fp8 logits", min_exact=0.60,
+                max_outside={"decode": 36, "logits": 168}[mode])
 
 
 # ------------------------------------------------------------------ writer, metadata, plans
@@ -245,11 +249,11 @@ def test_full_decode_b64_ctx128k_fp8_cache():
     bs, _ = run_gpu(inp)
     torch.cuda.synchronize()
     assert torch.isfinite(bs).all()
-    rows = np.array([0, 63], np.int32)
-    ref = oracle_run(inp, rows=rows, want_logits=True, compact=True)
-    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    rows = np.sort(np.random.default_rng(90).choice(64, 16, replace=False)).astype(np.int32)
+    ref = oracle_run(inp, rows=rows, want_logits=False, compact=True)
+    mb = ref.block_mags
     got = bs[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
-    compare(got, ref.blocks, mb, S, what="fp8-cache decode block scores (2 sampled requests)", **FP8)
+    compare(got, ref.blocks, mb, S, what=f"fp8-cache decode block scores ({len(rows)} sampled requests)", **FP8)
     compare_argmax(got, ref.blocks, mb, S, "fp8-cache decode block scores")
     del bs, inp
     torch.cuda.empty_cache()
@@ -263,11 +267,11 @@ def test_full_prefill_q4096_ctx128k_fp8_cache():
     torch.cuda.synchronize()
     # every row sees the 126976-token prefix: pages 0..991 are finite everywhere
     assert torch.isfinite(bs[:, :, :992]).all()
-    rows = np.array([0, 2047, 4095], np.int32)
-    ref = oracle_run(inp, rows=rows, want_logits=True, compact=True)
-    mb = block_mags(ref.mags, wl.page_size, wl.NB)
+    rows = _sample_rows(wl, 16, 91)
+    ref = oracle_run(inp, rows=rows, want_logits=False, compact=True)
+    mb = ref.block_mags
     got = bs[torch.as_tensor(rows, dtype=torch.long, device="cuda")].cpu().numpy()
-    compare(got, ref.blocks, mb, S, what="fp8-cache prefill block scores (3 sampled rows)", **FP8)
+    compare(got, ref.blocks, mb, S, what=f"fp8-cache prefill block scores ({len(rows)} sampled rows)", **FP8)
     compare_argmax(got, ref.blocks, mb, S, "fp8-cache prefill block scores")
     del bs, inp
     torch.cuda.empty_cache()
