@@ -1,22 +1,33 @@
 """Benchmark of the paged MXFP4 index scorer on one MI355X.
 
-Default workload: decode, B = 64 requests, one query row each, context
-131072 (1024 pages of 128 tokens per request), H = 64, D = 128, bf16 query
-~ N(0, 1), e2m1 codes uniform, e8m0 bytes uniform in [122, 127], pages drawn
-without replacement from a 300k-page pool (2.6 GB). A step is one scorer
-call over the whole batch; four disjoint block tables rotate between steps
-so consecutive calls read different pages (the pool defeats the 256 MB
-last-level cache). Inputs are resident in HBM before timing starts.
+Default run: the five scorer workloads, each with inputs resident in HBM
+before any timing starts:
+  1 prefill_q64_ctx1k          64 query rows after a 960-token prefix, logits
+                               + block scores, 16-page pool;
+  2 decode_b64_ctx128k         B = 64 decode rows, context 131072, pages drawn
+                               from a 300k-page pool (2.6 GB);
+  3 prefill_q4096_ctx128k      4096 rows after prefix 126976, e4m3 query;
+  4 prefill_chunk32k_ctx132768 32768 rows after prefix 100000, one e8m0 byte
+                               per token in 100..150 (the headline: the largest);
+  5 logits_b8_q128_ctx8k_shared per-head logits, 64-token pages in a shared
+                               two-slot pool past byte 4.608e9.
+H = 64, D = 128, bf16 query ~ N(0, 1) unless stated, e2m1 codes uniform,
+e8m0 bytes uniform in [122, 127] unless stated. Workloads beyond the smallest
+rotate four disjoint block tables between steps so consecutive calls read
+different pages.
 
-Prints one JSON line (stdout). Throughput is live scored (row x head x token)
-triples per second; the line also carries us/call, achieved HBM GB/s and
-scaled-MFMA utilisation, the roofline of the dominant kernel and the CPU
-oracle's rate on a bounded sample of the same workload.
+Timing (the pages' method: graph replay, medians, two rounds with the order
+reversed): per workload W untimed warmup steps, then K steps captured once in
+a HIP graph; each round replays every workload's graph R times, the second
+round in reverse workload order; HIP events on the replay stream bracket
+each replay, so a step's time is its kernel's average launch duration. The
+reported time is the median over all replays of both rounds.
 
-The K timed steps are captured once in a HIP graph and replayed, so the
-host's launch overhead is not part of the time; HIP events on the replay
-stream bracket the replay. Each step is one kernel launch, so the per-step
-time is the kernel's average launch duration (--eager times plain launches).
+Prints one JSON line (stdout): the headline workload's figures at the top
+level (throughput = live scored (row x head x token) triples per second,
+us/call, achieved HBM GB/s and scaled-MFMA rate, the roofline of its kernel,
+the CPU oracle's rate on a bounded sample) and the same record for every
+workload under "workloads".
 
 HBM traffic: `--copy-probe` adds a plain 1 GiB float32 negation (reads and
 writes 2^30 bytes) ahead of the warmup, so that one `rocprofv3 --pmc
@@ -25,13 +36,12 @@ of known size; `--pmc-summary DB...` turns the two runs' databases into a
 traffic file (counter readings scaled by known bytes / copy reading), which
 the roofline picks up while the kernel sources still hash the same.
 
---config selects another workload (1: prefill 64 rows ctx 1k with logits,
-3: prefill 4096 rows ctx 128k e4m3, 4: chunked prefill 32768 rows ctx 132768,
-5: logits, 64-token pages in a shared pool past 4.608e9 bytes, 6: top-64 page
-selection over the block scores of config 3, 7: writing 2^20 bf16 keys into
-MXFP4 page slots; 8, 9, 10: configs 2, 3 and 7 over an fp8 (e4m3, 128 B per
-token) index cache, the format the MXFP4 one replaces; 11: paged MXFP4
-attention decode, 2048 rows x 16 query heads over 2048 tokens of K and V).
+--config N runs one workload instead (profiling): 1-5 as above, 6: top-64
+page selection over the block scores of config 3, 7: writing 2^20 bf16 keys
+into MXFP4 page slots; 8, 9, 10: configs 2, 3 and 7 over an fp8 (e4m3, 128 B
+per token) index cache, the format the MXFP4 one replaces; 11: paged MXFP4
+attention decode, 2048 rows x 16 query heads over 2048 tokens of K and V;
+12: config 4 with an e8m0 byte per (token, 32-element block).
 """
 from __future__ import annotations
 
@@ -171,15 +181,232 @@ def algorithmic_bytes(wl, inp) -> int:
     return kbytes + qbytes + table + out + meta
 
 
+SUITE = (1, 2, 3, 4, 5)            # the default run: the five scorer workloads
+HEADLINE = 4                        # the largest one carries the top-level line
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Case:
+    """One workload on the GPU: inputs resident in HBM, its plan and outputs,
+    and the K timed steps captured once in a HIP graph."""
+
+    def __init__(self, cfg: int, args, dev):
+        import torch
+        import mxfp4_paged_cache_amd as mx
+        from mxfp4_paged_cache_amd import workloads as W
+        self.cfg = cfg
+        wl = W.CONFIGS[cfg]()
+        # consecutive calls read disjoint page sets (the decode pool is larger
+        # than the 256 MB last-level cache; the prefill pages are not, and are
+        # rotated all the same)
+        if wl.mode == "decode" or wl.T * wl.H > 64 * 64:
+            wl.tables = 4
+        self.wl = wl
+        log(f"workload {wl.name}: generating inputs on the GPU")
+        t0 = time.time()
+        inp = W.make_inputs(wl, args.seed, dev)
+        torch.cuda.synchronize()
+        log(f"inputs ready in {time.time() - t0:.1f}s")
+        self.inp = inp
+        T, H, P = wl.T, wl.H, wl.page_size
+        NB, Wd = wl.NB, wl.window
+        S = W.INV_SQRT_D
+        bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if (wl.want_blocks and not wl.attn_group) else None
+        lg = torch.empty((T, H, Wd), dtype=torch.float32, device=dev) if wl.want_logits else None
+        self.bs, self.lg = bs, lg
+        plan = None
+        if not wl.attn_group:
+            plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks,
+                                k_dtype=wl.k_dtype)
+            log(f"plan: {plan.as_dict()}")
+        self.plan = plan
+        ao = torch.empty((T, H * wl.attn_group, 128), dtype=torch.bfloat16, device=dev) if wl.attn_group else None
+        sel = None
+        if wl.select_k:
+            # the selection's input: this prefill's block scores, computed once before timing
+            mx.score_prefill(inp.q, inp.k_data, inp.k_scale, inp.block_tables[0], inp.cu_seqlens_q, inp.seq_lens,
+                             inp.prefix_lens, max(wl.q_lens), Wd, S, out=bs, plan=plan)
+            sel = torch.empty((T, H, wl.select_k), dtype=torch.int32, device=dev)
+        wk = wslots = None
+        if wl.write_tokens:
+            # keys N(0,1) in bf16; whole pages in a seeded random page order
+            g = torch.Generator(device=dev)
+            g.manual_seed(args.seed * 1000003 + 77)
+            wk = torch.randn((wl.write_tokens, 128), generator=g, device=dev).to(torch.bfloat16)
+            npages = wl.write_tokens // P
+            pages = torch.randperm(wl.pool_pages, generator=g, device=dev)[:npages]
+            wslots = (pages[:, None] * P + torch.arange(P, device=dev)[None, :]).reshape(-1).to(torch.int64)
+        self.wk, self.wslots = wk, wslots
+
+        def call(i):
+            bt = inp.block_tables[i % len(inp.block_tables)]
+            if wl.attn_group:
+                mx.attn_decode(inp.q, inp.k_data, inp.k_scale, inp.extras["v_data"], inp.extras["v_scale"], bt,
+                               inp.seq_lens, Wd, S, out=ao)
+            elif wl.write_tokens:
+                mx.write_pages(wk, wslots, inp.k_data, inp.k_scale)
+            elif wl.select_k:
+                mx.select_pages(bs, wl.select_k, inp.seq_lens, Wd, P, cu_seqlens_q=inp.cu_seqlens_q,
+                                prefix_lens=inp.prefix_lens, out=sel)
+            elif wl.mode == "decode":
+                mx.score_decode(inp.q, inp.k_data, inp.k_scale, bt, inp.seq_lens, Wd, S, out=bs,
+                                logits=lg if lg is not None else False, plan=plan)
+            elif wl.mode == "logits":
+                mx.score_logits(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                                max(wl.q_lens), Wd, S, out=lg, block_scores=bs if bs is not None else False, plan=plan)
+            else:
+                mx.score_prefill(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
+                                 max(wl.q_lens), Wd, S, out=bs, logits=lg if lg is not None else False, plan=plan)
+        self.call = call
+        self.graph = None
+        self.replay_ms = {}            # round -> [ms per step of each replay]
+
+    def warm_and_capture(self, warmup: int, steps: int, eager: bool, dev):
+        import torch
+        for i in range(warmup):
+            self.call(i)
+        torch.cuda.synchronize()
+        if eager:
+            return
+        # capture the K timed steps once (side stream warm-up first, as capture requires)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            self.call(0)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(steps):
+                self.call(i)
+        torch.cuda.synchronize()
+
+    def time_replays(self, rnd: int, replays: int, steps: int, dev):
+        """`replays` timed runs of the K steps (a graph replay, or K eager
+        launches), each between two HIP events on the stream the kernels run
+        on; per-step times (ms) go to self.replay_ms[rnd]."""
+        import torch
+        stream = torch.cuda.current_stream(dev)   # the launches (or the replay) run on this stream
+        out = self.replay_ms.setdefault(rnd, [])
+        for _ in range(replays):
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            if self.graph is not None:
+                self.graph.replay()
+            else:
+                for i in range(steps):
+                    self.call(i)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1) / steps)   # one kernel launch per step
+
+    def record(self, args, with_cpu: bool):
+        """The workload's measurement record (the median over every replay of
+        both rounds; each round's median alongside)."""
+        import numpy as np
+        wl, inp = self.wl, self.inp
+        allms = [m for r in sorted(self.replay_ms) for m in self.replay_ms[r]]
+        ms = float(np.median(allms))
+        # live (row, query head, token) triples; attention counts every query head of every kv head
+        triples = wl.live_triples() * (wl.attn_group or 1)
+        # throughput: scored (row, head, token) triples/s; the selection consumes (row, head, page) block scores
+        units = wl.write_tokens if wl.write_tokens else (wl.T * wl.H * wl.NB if wl.select_k else triples)
+        value = units / (ms / 1e3)
+        abytes = algorithmic_bytes(wl, inp)
+        flops = (4.0 if wl.attn_group else 2.0) * 128 * triples   # attention: Q.K and P.V
+        gbps = abytes / (ms / 1e3) / 1e9
+        tflops = flops / (ms / 1e3) / 1e12
+        hbm_bound = (wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k) or
+                     bool(wl.write_tokens))
+        traffic = None
+        tpath = args.traffic or traffic_path(wl)
+        if os.path.exists(tpath):
+            with open(tpath) as f:
+                tr = json.load(f)
+            # counters taken on other kernel code no longer describe this kernel
+            if tr.get("workload") == wl.name and tr.get("source_hash") == kernel_source_hash(kernel_name(wl)):
+                traffic = tr.get("bytes_per_launch")
+        if hbm_bound:
+            roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+        cpu = None
+        if with_cpu:
+            if wl.attn_group:
+                cpu = cpu_baseline_attn(wl, inp, args.cpu_sample)
+            elif wl.write_tokens:
+                cpu = cpu_baseline_write(wl, self.wk, self.wslots, args.cpu_sample)
+            elif wl.select_k:
+                cpu = cpu_baseline_select(wl, self.bs, inp, args.cpu_sample)
+            else:
+                cpu = cpu_baseline(wl, inp, args.cpu_sample, args.cpu_seconds)
+        return {
+            "value": value,
+            "unit": "tokens/s" if wl.write_tokens else (
+                "(row\u00d7head\u00d7page)/s" if wl.select_k else "(row\u00d7head\u00d7token)/s"),
+            "ms_per_step": ms,
+            "us_per_call": ms * 1e3,
+            "timing": {"stat": "median of every replay of both rounds", "replays": len(allms),
+                       "steps_per_replay": args.steps,
+                       "graph": self.graph is not None,
+                       "round_median_us": {str(r): round(float(np.median(v)) * 1e3, 3)
+                                           for r, v in sorted(self.replay_ms.items())},
+                       "min_us": round(min(allms) * 1e3, 3), "max_us": round(max(allms) * 1e3, 3)},
+            "dtype": path_dtype(wl),
+            "config": workload_config(wl, inp),
+            "hbm_gbps": round(gbps, 1),
+            "mfma_tflops": None if (wl.select_k or wl.write_tokens) else round(tflops, 2),
+            "mfma_util_fp8_rate": None if (wl.select_k or wl.write_tokens or wl.attn_group) else round(
+                tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+            "algorithmic_bytes": abytes,
+            "live_triples": None if (wl.select_k or wl.write_tokens) else triples,
+            "roofline": roof,
+            "cpu_baseline": cpu,
+            "kernel": kernel_name(wl),
+        }
+
+
+def workload_config(wl, inp) -> dict:
+    return {"workload": wl.name, "batch": wl.B, "query_rows": wl.T, "heads": wl.H, "head_dim": 128,
+            "page_size": wl.page_size, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype, "cache": wl.k_dtype,
+            "e8m0_range": [wl.scale_lo, wl.scale_hi],
+            **({"e8m0_per": "token" if wl.scale_mode == "token" else "32-element block"}
+               if wl.k_dtype == "mxfp4" else {}),
+            "outputs": "attention" if wl.attn_group else (("block_scores" if wl.want_blocks else "") +
+                                                          ("+logits" if wl.want_logits else "")),
+            "rotating_tables": len(inp.block_tables),
+            **({"select_k": wl.select_k} if wl.select_k else {}),
+            **({"write_tokens": wl.write_tokens} if wl.write_tokens else {}),
+            **({"query_heads_per_kv_head": wl.attn_group} if wl.attn_group else {})}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20, help="steps per timed replay (K)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed warmup steps per workload (W)")
+    ap.add_argument("--replays", type=int, default=5, help="timed replays per workload per round")
+    ap.add_argument("--rounds", type=int, default=2, help="rounds of replays; every other round in reverse order")
+    ap.add_argument("--config", type=int, default=0,
+                    help="one workload (1-12) instead of the five scorer workloads (profiling runs)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="rows the oracle scores for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0, help="oracle work per CPU-baseline sample")
     ap.add_argument("--traffic", type=str, default="", help="traffic file (default: the one under profiles/)")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of a graph replay")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB copy kernel first (counter calibration)")
@@ -189,7 +416,7 @@ def main():
 
     if args.pmc_summary:
         from mxfp4_paged_cache_amd import workloads as W
-        wl = W.CONFIGS[args.config]()
+        wl = W.CONFIGS[args.config or HEADLINE]()
         rec = pmc_summary(args.pmc_summary).get(kernel_name(wl), {})
         rec = {"workload": wl.name, "kernel": kernel_name(wl), "source_hash": kernel_source_hash(kernel_name(wl)),
                "copy_probe_bytes": COPY_PROBE_BYTES, **rec}
@@ -204,11 +431,9 @@ def main():
               f"heads or context pages split across GPUs with no exchange step", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import mxfp4_paged_cache_amd as mx
-    from mxfp4_paged_cache_amd import workloads as W
 
     if not os.path.exists(mx.library_path()):
         from mxfp4_paged_cache_amd import build as mxbuild
@@ -218,63 +443,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl = W.CONFIGS[args.config]()
-    if wl.mode == "decode":
-        wl.tables = 4
-    log(f"workload {wl.name}: generating inputs on the GPU")
-    t0 = time.time()
-    inp = W.make_inputs(wl, args.seed, dev)
-    torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f}s")
-    T, H, P = wl.T, wl.H, wl.page_size
-    NB, Wd = wl.NB, wl.window
-    S = W.INV_SQRT_D
-
-    bs = torch.empty((T, H, NB), dtype=torch.float32, device=dev) if (wl.want_blocks and not wl.attn_group) else None
-    lg = torch.empty((T, H, Wd), dtype=torch.float32, device=dev) if wl.want_logits else None
-    plan = None
-    if not wl.attn_group:
-        plan = mx.make_plan(wl.mode, inp.q.dtype, P, H, wl.B, max(wl.q_lens), Wd, wl.want_logits, wl.want_blocks,
-                            k_dtype=wl.k_dtype)
-        log(f"plan: {plan.as_dict()}")
-    ao = torch.empty((T, H * wl.attn_group, 128), dtype=torch.bfloat16, device=dev) if wl.attn_group else None
-
-    sel = None
-    if wl.select_k:
-        # the selection's input: this prefill's block scores, computed once before timing
-        mx.score_prefill(inp.q, inp.k_data, inp.k_scale, inp.block_tables[0], inp.cu_seqlens_q, inp.seq_lens,
-                         inp.prefix_lens, max(wl.q_lens), Wd, S, out=bs, plan=plan)
-        sel = torch.empty((T, H, wl.select_k), dtype=torch.int32, device=dev)
-
-    wk = wslots = None
-    if wl.write_tokens:
-        # keys N(0,1) in bf16; whole pages in a seeded random page order
-        g = torch.Generator(device=dev)
-        g.manual_seed(args.seed * 1000003 + 77)
-        wk = torch.randn((wl.write_tokens, 128), generator=g, device=dev).to(torch.bfloat16)
-        npages = wl.write_tokens // P
-        pages = torch.randperm(wl.pool_pages, generator=g, device=dev)[:npages]
-        wslots = (pages[:, None] * P + torch.arange(P, device=dev)[None, :]).reshape(-1).to(torch.int64)
-
-    def call(i):
-        bt = inp.block_tables[i % len(inp.block_tables)]
-        if wl.attn_group:
-            mx.attn_decode(inp.q, inp.k_data, inp.k_scale, inp.extras["v_data"], inp.extras["v_scale"], bt,
-                           inp.seq_lens, Wd, S, out=ao)
-        elif wl.write_tokens:
-            mx.write_pages(wk, wslots, inp.k_data, inp.k_scale)
-        elif wl.select_k:
-            mx.select_pages(bs, wl.select_k, inp.seq_lens, Wd, P, cu_seqlens_q=inp.cu_seqlens_q,
-                            prefix_lens=inp.prefix_lens, out=sel)
-        elif wl.mode == "decode":
-            mx.score_decode(inp.q, inp.k_data, inp.k_scale, bt, inp.seq_lens, Wd, S, out=bs,
-                            logits=lg if lg is not None else False, plan=plan)
-        elif wl.mode == "logits":
-            mx.score_logits(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
-                            max(wl.q_lens), Wd, S, out=lg, block_scores=bs if bs is not None else False, plan=plan)
-        else:
-            mx.score_prefill(inp.q, inp.k_data, inp.k_scale, bt, inp.cu_seqlens_q, inp.seq_lens, inp.prefix_lens,
-                             max(wl.q_lens), Wd, S, out=bs, logits=lg if lg is not None else False, plan=plan)
+    cfgs = (args.config,) if args.config else SUITE
+    head = args.config or HEADLINE
+    cases = {c: Case(c, args, dev) for c in cfgs}
 
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
@@ -284,111 +455,50 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-    graph = None
-    if not args.eager:
-        # capture the K timed steps once (side stream warm-up first, as capture requires)
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            call(0)
-        torch.cuda.current_stream(dev).wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                call(i)
-        torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)   # the launches (or the replay) run on this stream
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    for c in cfgs:
+        cases[c].warm_and_capture(args.warmup, args.steps, args.eager, dev)
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            call(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    for rnd in range(args.rounds):
+        order = cfgs if rnd % 2 == 0 else tuple(reversed(cfgs))
+        for c in order:
+            cases[c].time_replays(rnd, args.replays, args.steps, dev)
+        log(f"round {rnd}: " + ", ".join(f"{cases[c].wl.name} {cases[c].replay_ms[rnd][-1] * 1e3:.1f} us"
+                                          for c in cfgs))
     wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms = ms_total / args.steps   # one kernel launch per step: this is the launch's average duration
 
-    # live (row, query head, token) triples; attention counts every query head of every kv head
-    triples = wl.live_triples() * (wl.attn_group or 1)
-    # throughput: scored (row, head, token) triples/s; the selection consumes (row, head, page) block scores
-    units = wl.write_tokens if wl.write_tokens else (wl.T * wl.H * wl.NB if wl.select_k else triples)
-    value = units / (ms / 1e3)
-    abytes = algorithmic_bytes(wl, inp)
-    flops = (4.0 if wl.attn_group else 2.0) * 128 * triples   # attention: Q.K and P.V
-    gbps = abytes / (ms / 1e3) / 1e9
-    tflops = flops / (ms / 1e3) / 1e12
-    hbm_bound = (wl.mode in ("decode", "logits") or (wl.T * wl.H <= 64 * 64) or bool(wl.select_k) or
-                 bool(wl.write_tokens))
-    traffic = None
-    tpath = args.traffic or traffic_path(wl)
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        # counters taken on other kernel code no longer describe this kernel
-        if tr.get("workload") == wl.name and tr.get("source_hash") == kernel_source_hash(kernel_name(wl)):
-            traffic = tr.get("bytes_per_launch")
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        if wl.attn_group:
-            cpu = cpu_baseline_attn(wl, inp, args.cpu_sample)
-        elif wl.write_tokens:
-            cpu = cpu_baseline_write(wl, wk, wslots, args.cpu_sample)
-        elif wl.select_k:
-            cpu = cpu_baseline_select(wl, bs, inp, args.cpu_sample)
-        else:
-            cpu = cpu_baseline(wl, inp, args.cpu_sample)
-
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+    recs = {}
+    for c in cfgs:
+        recs[c] = cases[c].record(args, not args.no_cpu_baseline)
+        log(f"{cases[c].wl.name}: {recs[c]['us_per_call']:.1f} us, roofline {recs[c]['roofline']['frac']}")
+    top = recs[head]
     line = {
         "metric": "\u00b5s/call and scored (row\u00d7head\u00d7token)/s; HBM GB/s + scaled-MFMA util vs peak",
-        "value": value,
-        "unit": "tokens/s" if wl.write_tokens else (
-            "(row\u00d7head\u00d7page)/s" if wl.select_k else "(row\u00d7head\u00d7token)/s"),
+        "value": top["value"],
+        "unit": top["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
-        "us_per_call": ms * 1e3,
+        "ms_per_step": top["ms_per_step"],
+        "us_per_call": top["us_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": path_dtype(wl),
+        "dtype": top["dtype"],
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.B, "query_rows": T, "heads": H, "head_dim": 128,
-                   "page_size": P, "context": max(wl.seq_lens), "q_dtype": wl.q_dtype, "cache": wl.k_dtype,
-                   "e8m0_range": [wl.scale_lo, wl.scale_hi],
-                   "outputs": "attention" if wl.attn_group else (("block_scores" if wl.want_blocks else "") +
-                                                                  ("+logits" if wl.want_logits else "")), "rotating_tables": len(inp.block_tables),
-                   **({"select_k": wl.select_k} if wl.select_k else {}),
-                   **({"write_tokens": wl.write_tokens} if wl.write_tokens else {}),
-                   **({"query_heads_per_kv_head": wl.attn_group} if wl.attn_group else {})},
-        "hbm_gbps": round(gbps, 1),
-        "mfma_tflops": None if (wl.select_k or wl.write_tokens) else round(tflops, 2),
-        "mfma_util_fp8_rate": None if (wl.select_k or wl.write_tokens or wl.attn_group) else round(
-            tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-        "algorithmic_bytes": abytes,
-        "live_triples": None if (wl.select_k or wl.write_tokens) else triples,
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "wall_s_timed": round(wall, 4),
-        "timing": "eager launches" if graph is None else "graph replay of the timed steps",
-        "kernel": kernel_name(wl),
+        "config": top["config"],
+        "hbm_gbps": top["hbm_gbps"],
+        "mfma_tflops": top["mfma_tflops"],
+        "mfma_util_fp8_rate": top["mfma_util_fp8_rate"],
+        "algorithmic_bytes": top["algorithmic_bytes"],
+        "live_triples": top["live_triples"],
+        "roofline": top["roofline"],
+        "cpu_baseline": top["cpu_baseline"],
+        "timing": top["timing"],
+        "kernel": top["kernel"],
+        "host": {"cpu_model": cpu_model(), "threads": threads},
+        "wall_s_timed": round(wall, 3),
+        "workloads": {cases[c].wl.name: recs[c] for c in cfgs},
     }
     print(json.dumps(line), flush=True)
 
@@ -462,7 +572,7 @@ def cpu_baseline_select(wl, bs, inp, sample_rows: int):
             "sample": f"{len(rows)} of {wl.T} rows, all heads and pages ({n} block scores), {dt:.2f} s"}
 
 
-def cpu_baseline(wl, inp, sample_rows: int):
+def cpu_baseline(wl, inp, sample_rows: int, seconds: float = 6.0):
     """The oracle (test infrastructure, untuned) on a bounded sample of the same
     workload, timed on this host's cores; reported as triples/s."""
     import numpy as np
@@ -473,10 +583,10 @@ def cpu_baseline(wl, inp, sample_rows: int):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
     T = wl.T
     if sample_rows <= 0:
-        # about 10 s of oracle work: ~7e6 live triples per core-second measured
-        # for this oracle, so ~1.1e9 triples on 16 cores
+        # about `seconds` of oracle work: ~7e6 live triples per core-second
+        # measured for this oracle (~6.7e8 triples in 6 s on 16 cores)
         per_row = max(1, (sum(wl.limits()) * wl.H) // max(T, 1))
-        budget = int(7e6 * threads * 10)
+        budget = int(7e6 * threads * seconds)
         sample_rows = max(1, min(T, budget // per_row))
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(T, size=min(sample_rows, T), replace=False)).astype(np.int32)
@@ -506,6 +616,7 @@ def cpu_baseline(wl, inp, sample_rows: int):
                  want_logits=wl.want_logits, want_blocks=wl.want_blocks, num_threads=threads, k_dtype=wl.k_dtype)
     dt = time.perf_counter() - t0
     return {"value": sample_triples / dt, "unit": "(row\u00d7head\u00d7token)/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(rows)} of {T} query rows ({sample_triples} live triples, all heads and pages of "
                       f"those rows), {dt:.2f} s"}
 
