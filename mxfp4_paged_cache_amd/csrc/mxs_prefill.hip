@@ -30,49 +30,68 @@ constexpr int kFlushLanesPerRow = kPrefillStagePages / 4;     // 4 pages per lan
 
 // Score one LDS-resident page against this wave's query tiles; r[n] gets the
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
-// The 16-token tiles run in a real (not unrolled) loop, two per trip, so at
-// most two tiles of MFMA results are live.
+//
+// Software-pipelined over the page's 16-token tiles: a step
+// reads the next tile's K operand from LDS, then issues the NQ MFMAs of tile
+// t, each followed by the fold (two v_max3) of the matching result of tile
+// t - 1. A fold thus reads a result written NQ MFMAs earlier, past the
+// MFMA-to-VALU hazard window, so no wait states sit between them (with each
+// fold right behind its own MFMA, every other MFMA was padded with 9 wait
+// states). Two result sets alternate between the halves of a loop trip, so
+// only two tiles of results are live and none is copied.
 template <int KDT, int P, int NQ, bool MASK>
 __device__ __forceinline__ void prefill_page(const uint8_t* kb, const v8i (&qt)[NQ], const int (&lrel)[NQ], int g,
                                              int i, float (&r)[NQ]) {
   constexpr int TPP = P / 16;
+  // The masked and unmasked variants begin alike (the first tile is not
+  // folded yet); this marker keeps the compiler from hoisting that common
+  // start above the branch between them, which left the first tile's results
+  // in registers the unmasked loop then had to copy out of (32 moves a page).
+  asm volatile("; prefill page, mask %0" ::"n"(MASK ? 1 : 0));
   float m[NQ];
 #pragma unroll
   for (int n = 0; n < NQ; ++n) m[n] = kNegInf;
-  auto mma = [&](const KTile<KDT>& k, v4f (&c)[NQ]) {
+  auto fold1 = [&](int t, int n, v4f c) {
+    if constexpr (MASK) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) c[n] = mma_tile(k, qt[n]);
+      for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel[n]) ? c[v] : kNegInf;
+    }
+    m[n] = max_into(m[n], c);
   };
-  auto fold = [&](int t, const v4f (&cc)[NQ]) {
+  // tile t's MFMAs into cur, interleaved with the folds of tile t - 1 (prev)
+  // when there is one; the next tile's K reads go first
+  auto step = [&](int t, const KTile<KDT>& k, v4f (&cur)[NQ], const v4f (&prev)[NQ]) {
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-      v4f c = cc[n];
-      if constexpr (MASK) {
+      cur[n] = mma_tile(k, qt[n]);
+      if (t > 0) fold1(t - 1, n, prev[n]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                     // LDS reads of the next tile
 #pragma unroll
-        for (int v = 0; v < 4; ++v) c[v] = (16 * t + v < lrel[n]) ? c[v] : kNegInf;
-      }
-      m[n] = max_into(m[n], c);
+    for (int n = 0; n < NQ; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+      if (t > 0) __builtin_amdgcn_sched_group_barrier(0x002, MASK ? 6 : 2, 0);   // one fold
     }
   };
-  // Two tiles per trip and nothing carried across trips: the trip's K tiles
-  // are read from LDS at its top (the other wave on the SIMD covers the LDS
-  // latency). Prefetching the next pair into the loop-carried registers
-  // instead cost one register copy per two MFMAs and measured 2% slower.
+  v4f cA[NQ], cB[NQ];
   // The wave issues its MFMAs at raised priority, so that of the two waves
   // sharing a SIMD the one with matrix work goes first (measured 1-2% on
   // both block-score workloads).
   __builtin_amdgcn_s_setprio(1);
+  KTile<KDT> kA = lds_tile<KDT, P>(kb, g, i, 0);
+  KTile<KDT> kB = lds_tile<KDT, P>(kb, g, i, 1);
+  step(0, kA, cA, cB);
 #pragma unroll 1
-  for (int t = 0; t < TPP; t += 2) {
-    const KTile<KDT> k0 = lds_tile<KDT, P>(kb, g, i, t);
-    const KTile<KDT> k1 = lds_tile<KDT, P>(kb, g, i, t + 1);
-    v4f cA[NQ], cB[NQ];
-    mma(k0, cA);
-    mma(k1, cB);
-    fold(t, cA);
-    fold(t + 1, cB);
+  for (int t = 1; t < TPP - 1; t += 2) {
+    kA = lds_tile<KDT, P>(kb, g, i, t + 1);
+    step(t, kB, cB, cA);
+    kB = lds_tile<KDT, P>(kb, g, i, t + 2);
+    step(t + 1, kA, cA, cB);
   }
+  step(TPP - 1, kB, cB, cA);
   __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) fold1(TPP - 1, n, cB[n]);
 #pragma unroll
   for (int n = 0; n < NQ; ++n) r[n] = fold_groups(m[n]);
 }
