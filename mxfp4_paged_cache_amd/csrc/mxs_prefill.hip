@@ -14,8 +14,9 @@ using namespace dev;
 // heads of one row when H is a multiple of 16. Each wave keeps 8 query tiles
 // in registers for the whole item; every page is staged once per workgroup in
 // LDS (double-buffered, 8.5 KB per buffer at P = 128 for MXFP4, 16 KB for an
-// fp8 cache) and read by all four waves. Block scores are staged in LDS for up to 16 pages and leave as
-// contiguous per-slot rows.
+// fp8 cache) and read by all four waves. Block scores are staged in an LDS
+// ring of 16 pages per slot and leave as 64-byte-aligned segments of each
+// output row (see the flush below).
 //
 // Work items are ordered slot block fastest: at any moment the whole grid
 // works on one chunk of pages (small enough for every XCD's L2), and each
@@ -24,9 +25,9 @@ using namespace dev;
 // workgroup the same.
 // ---------------------------------------------------------------------------
 constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;   // query slots per work item
-constexpr int kPrefillStagePages = 16;                        // pages per block-score flush
-constexpr int kPrefillStageStride = kPrefillStagePages + 1;   // LDS row pitch (odd: no bank conflicts)
-constexpr int kFlushLanesPerRow = kPrefillStagePages / 4;     // 4 pages per lane
+constexpr int kWaveSlots = kPrefillTiles * 16;                // query slots per wave
+constexpr int kRingPages = 16;                                // block scores per slot in the LDS ring: 64 bytes
+constexpr int kPrefillStageStride = kRingPages + 1;           // LDS row pitch (odd: no bank conflicts)
 
 // Score one LDS-resident page against this wave's query tiles; r[n] gets the
 // (unscaled) max over the page's live tokens for slot (tile n, lane i).
@@ -102,10 +103,19 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
   constexpr int PB = kStagedPageBytes<KDT, P>;   // bytes of one staged page
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * PB];
   __shared__ float stage[kPrefillSlots * kPrefillStageStride];
+  // Block-score flush bookkeeping, per wave: the output row of each of its
+  // slots (address of page 0) and, per page phase e, the slots whose 64-byte
+  // output segments end at pages j with j % 16 == e.
+  __shared__ uint64_t frow_all[kWaves][kWaveSlots];
+  __shared__ uint8_t flist_all[kWaves][kRingPages][kWaveSlots];
+  __shared__ uint32_t fcount_all[kWaves][kRingPages];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   const float s = a.sm_scale;
+  uint64_t* frow = frow_all[wave];
+  uint32_t* fcount = fcount_all[wave];
+  float* ring = stage + wave * kWaveSlots * kPrefillStageStride;
 
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
     const int sb = (int)(item % a.slot_items);
@@ -144,6 +154,52 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     const int jl = min(j1, (item_lim + P - 1) / P);   // pages [j0, jl) hold live tokens
     const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
 
+    // Output rows of this wave's slots and the phase at which each row's
+    // 64-byte segments end: row element j (page j) sits at float index
+    // ax + j, so a segment ends at every page j with (ax + j + 1) % 16 == 0.
+    // The slots are bucketed by that phase, so each page's flush touches
+    // only the rows that complete a segment there.
+    const int wslots = (int)min((int64_t)kWaveSlots, max((int64_t)0, nslots - sbeg - (int64_t)wave * kWaveSlots));
+    {
+      const uint32_t slot0 = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H));   // slot sbeg within its row
+      const int64_t rowb = (int64_t)row0 + sbeg / a.H;
+      wave_lds_sync();   // the last item's flush reads are done
+      if (lane < kRingPages) fcount[lane] = 0u;
+      wave_lds_sync();
+#pragma unroll
+      for (int half = 0; half < kWaveSlots / 64; ++half) {
+        const int sl = half * 64 + lane;
+        if (sl < wslots) {
+          const uint32_t slot = slot0 + (uint32_t)(wave * kWaveSlots + sl);
+          const uint32_t dr = slot / (uint32_t)a.H;
+          float* rp = a.bs + (rowb + dr) * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride;
+          frow[sl] = reinterpret_cast<uint64_t>(rp);
+          const uint32_t e = (0u - (uint32_t)(reinterpret_cast<uint64_t>(rp) >> 2) - 1u) & (kRingPages - 1);
+          const uint32_t pos = atomicAdd(&fcount[e], 1u);
+          flist_all[wave][e][pos] = (uint8_t)sl;
+        }
+      }
+      wave_lds_sync();
+    }
+    // Write the staged scores of slot sl for the pages of its current 64-byte
+    // segment (the one holding page j) from the item's first page on: lane
+    // quarter q writes pages w + 4q .. w + 4q + 3, one 16-byte store when all
+    // four are this item's.
+    auto flush_slot = [&](int sl, int j) {
+      float* rp = reinterpret_cast<float*>(frow[sl]);
+      const uint32_t ax = (uint32_t)(reinterpret_cast<uint64_t>(rp) >> 2);
+      const int p0 = j - (int)((ax + (uint32_t)j) & (kRingPages - 1)) + 4 * (lane & 3);
+      const float* src = ring + sl * kPrefillStageStride;
+      if (p0 >= j0 && p0 + 3 <= j) {
+        const v4f v = {src[p0 & 15], src[(p0 + 1) & 15], src[(p0 + 2) & 15], src[(p0 + 3) & 15]};
+        *reinterpret_cast<v4f*>(rp + p0) = v;
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (p0 + x >= j0 && p0 + x <= j) rp[p0 + x] = src[(p0 + x) & 15];
+      }
+    };
+
     // page ids, 64 at a time: lane l holds the id of page jid + l (one table
     // read per 64 pages, picked per page with readlane, so no page waits on
     // a table read before its loads can issue)
@@ -159,7 +215,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       stage_store<KDT, P>(st, kbuf, tid);
     }
     __syncthreads();
-    int jbase = j0;
     for (int j = j0; j < j1; ++j) {
       float r[NQ];
       if (j < jl) {
@@ -185,53 +240,25 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) r[n] = kNegInf;
       }
-      {
-        if (g == 0) {
+      if (g == 0) {
 #pragma unroll
-          for (int n = 0; n < NQ; ++n) stage[((wave * NQ + n) * 16 + i) * kPrefillStageStride + (j - jbase)] = r[n] * s;
-        }
-        if ((j + 1) % kPrefillStagePages == 0 || j == j1 - 1) {
-          // Each wave flushes its own slot rows [wave * 16 NQ, +16 NQ) for pages
-          // [jbase, j]; no other wave touches them, so no workgroup barrier is
-          // needed (a wave's LDS accesses complete in order; the fences keep the
-          // compiler from moving its reads above its writes). A group of TPR
-          // lanes writes one contiguous run of a row, 4 pages per lane; windows
-          // end at multiples of the window size, so in aligned rows a full
-          // window covers whole 64- or 128-byte lines.
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int npg = j - jbase + 1;
-          constexpr int TPR = kFlushLanesPerRow;
-          const int part = lane % TPR;
-          const int lo = wave * NQ * 16;
-          const int hi = (int)min((int64_t)lo + NQ * 16, nslots - sbeg);
-          const bool full = 4 * part + 3 < npg;
-          const bool v4 = a.vec_bs == 4 && (jbase & 3) == 0 && full;
-          const bool v2 = a.vec_bs >= 2 && (jbase & 1) == 0 && full;
-          const uint32_t slot0 = (uint32_t)(sbeg - (int64_t)(a.H) * (sbeg / a.H));   // slot sbeg within its row
-          const int64_t rowb = (int64_t)row0 + sbeg / a.H;
-          for (int sl = lo + lane / TPR; sl < hi; sl += 64 / TPR) {
-            if (4 * part >= npg) continue;
-            const uint32_t slot = slot0 + (uint32_t)sl;
-            const uint32_t dr = slot / (uint32_t)a.H;
-            float* dst = a.bs + (rowb + dr) * a.bs_row_stride + (int64_t)(slot - dr * (uint32_t)a.H) * a.bs_head_stride +
-                         jbase + 4 * part;
-            const float* src = stage + sl * kPrefillStageStride + 4 * part;
-            if (v4) {
-              const v4f v = {src[0], src[1], src[2], src[3]};
-              *reinterpret_cast<v4f*>(dst) = v;
-            } else if (v2) {
-              typedef float v2f __attribute__((ext_vector_type(2)));
-              const v2f v0 = {src[0], src[1]}, v1 = {src[2], src[3]};
-              reinterpret_cast<v2f*>(dst)[0] = v0;
-              reinterpret_cast<v2f*>(dst)[1] = v1;
-            } else {
-              for (int x = 0; x < 4 && 4 * part + x < npg; ++x) dst[x] = src[x];
-            }
-          }
-          jbase = j + 1;
-        }
+        for (int n = 0; n < NQ; ++n) ring[(n * 16 + i) * kPrefillStageStride + (j & (kRingPages - 1))] = r[n] * s;
+      }
+      // Each wave flushes its own slots' rows (no other wave touches them, so
+      // no workgroup barrier: a wave's LDS accesses complete in order, and
+      // the fences keep the compiler from moving its reads above its writes).
+      // A row's segment leaves when complete, as whole 64-byte-aligned
+      // pieces: with rows that are not 64-byte aligned (1038 floats each, say)
+      // fixed 16-page windows split every piece over two segments, and the
+      // chunked prefill took 4% longer than with aligned rows. On the item's
+      // last page every slot writes what is left of its segment.
+      wave_lds_sync();
+      if (j == j1 - 1) {
+        for (int sl = lane >> 2; sl < wslots; sl += 16) flush_slot(sl, j);
+      } else {
+        const uint32_t e = (uint32_t)j & (kRingPages - 1);
+        const int cnt = __builtin_amdgcn_readfirstlane((int)fcount[e]);
+        for (int k = lane >> 2; k < cnt; k += 16) flush_slot(flist_all[wave][e][k], j);
       }
       __syncthreads();
     }

@@ -203,6 +203,32 @@ def test_split_and_region_layouts_bitwise():
     assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
 
 
+@pytest.mark.parametrize("pad", [1, 3, 8, 13])
+def test_block_scores_into_strided_unaligned_rows(pad):
+    # Block-score rows starting at every 4-byte offset of a 64-byte segment
+    # (output views [T, H, NB] cut out of [T, H, NB + pad] at column `pad`):
+    # the block-score kernel writes each row in 64-byte-aligned segments, and
+    # the result must equal the contiguous output bit for bit, with nothing
+    # written outside the view; windows that end mid-segment and several
+    # page chunks per row included.
+    wl = W.Workload("strided_bs", "prefill", H=7, page_size=64, q_lens=[40, 3], prefix_lens=[2000, 90],
+                    seq_lens=[2040, 93], max_seq_len=2100)
+    host = W.make_inputs(wl, 30 + pad, "cpu")
+    dev = gpu_inputs(host)
+    NB = wl.NB
+    ref, _ = run_gpu(dev)
+    for pun in (0, 3):
+        base = torch.full((wl.T, wl.H, NB + pad), 7.0, device="cuda")
+        view = base[:, :, pad:]
+        p = mx.make_plan("prefill", torch.bfloat16, 64, wl.H, 2, 40, 2100, False, True, pun)
+        mx.score_prefill(dev.q, dev.k_data, dev.k_scale, dev.block_table, dev.cu_seqlens_q, dev.seq_lens,
+                         dev.prefix_lens, 40, 2100, S, out=view, plan=p)
+        torch.cuda.synchronize()
+        assert torch.equal(view.contiguous().view(torch.int32), ref.view(torch.int32)), (pad, pun)
+        assert bool((base[:, :, :pad] == 7.0).all()), (pad, pun)
+    say(f"  pad {pad}: strided block scores equal the contiguous ones")
+
+
 def test_explicit_plans_give_identical_outputs():
     wl = W.Workload("plans", "prefill", H=64, page_size=128, q_lens=[33, 12], prefix_lens=[900, 100],
                     seq_lens=[933, 112])
