@@ -275,6 +275,9 @@ constexpr int kNonTemporal = 2;   // cache-policy operand of a buffer load: nt (
 __device__ __forceinline__ u4 buffer_load16_nt(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
 }
+__device__ __forceinline__ uint32_t buffer_load4_nt(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNonTemporal);
+}
 __device__ __forceinline__ int buffer_load1_nt(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, kNonTemporal);
 }

@@ -6,8 +6,6 @@
 // ascending page order and padded with -1 (ATOM #2770, "How it works": the
 // selection follows the scorer; the sparse-attention commit: the tail page is
 // always selected; k and the tie rule are this library's reading).
-#include <type_traits>
-
 #include "mxs_device.h"
 
 namespace mxs {
@@ -63,55 +61,28 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) { return wave_reduce<true>(x); }
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) { return wave_reduce<false>(x); }
 
-// The same over finite floats (no NaN reaches them), as a uniform value.
-template <bool MIN>
-__device__ __forceinline__ float wave_reduce_f(float x) {
-  const int id = __float_as_int(MIN ? __builtin_inff() : -__builtin_inff());
-  auto op = [](float a, float b) { return MIN ? __builtin_fminf(a, b) : __builtin_fmaxf(a, b); };
-  auto dpp = [&](float v, auto ctrl, auto rmask) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), decltype(ctrl)::value,
-                                                      decltype(rmask)::value, 0xF, false));
-  };
-  using c111 = std::integral_constant<int, 0x111>;
-  using c112 = std::integral_constant<int, 0x112>;
-  using c114 = std::integral_constant<int, 0x114>;
-  using c118 = std::integral_constant<int, 0x118>;
-  using c142 = std::integral_constant<int, 0x142>;
-  using c143 = std::integral_constant<int, 0x143>;
-  using mF = std::integral_constant<int, 0xF>;
-  using mA = std::integral_constant<int, 0xA>;
-  using mC = std::integral_constant<int, 0xC>;
-  x = op(x, dpp(x, c111{}, mF{}));   // row_shr:1
-  x = op(x, dpp(x, c112{}, mF{}));   // row_shr:2
-  x = op(x, dpp(x, c114{}, mF{}));   // row_shr:4
-  x = op(x, dpp(x, c118{}, mF{}));   // row_shr:8
-  x = op(x, dpp(x, c142{}, mA{}));   // row_bcast:15
-  x = op(x, dpp(x, c143{}, mC{}));   // row_bcast:31
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
-// The scores of one (row, head), all loads issued together (indices past NB
-// read the last page's score and are then dropped, so no load is predicated).
-// An empty window (NB = 0) reads nothing: every page is then dead.
 // Blocks of 64 pages every row of NB pages fills when a kernel with PER
 // blocks per lane runs it: the launch picks the smallest PER in {4, 8, 16,
 // 32, 64} with 64 PER >= NB, so for PER >= 8 the first PER / 2 are full.
 template <int PER>
 constexpr int kFullBlocks = PER >= 8 ? PER / 2 : 0;
 
-// The full blocks load at fixed offsets from one lane address; the others
-// clamp to the last page (and are dropped as dead past NB).
+// The scores of one (row, head), all loads issued together, through buffer
+// resources that end at NB: a load past NB returns 0 without reading memory
+// (such pages are dropped as dead), so an empty window (NB = 0) reads nothing.
+// One resource per 16 blocks keeps every offset in the instruction's 12-bit
+// immediate, which the hardware's range check covers.
 template <int PER>
-__device__ __forceinline__ void load_scores(const SArgs& a, int64_t r, int h, int lane, float (&v)[PER]) {
-  if (a.NB <= 0) {
+__device__ __forceinline__ void load_scores(const float* srow, int NB, int lane, float (&v)[PER]) {
+  const uint32_t bytes = NB > 0 ? 4u * (uint32_t)NB : 0u;
 #pragma unroll
-    for (int m = 0; m < PER; ++m) v[m] = -__builtin_inff();
-    return;
+  for (int g = 0; g < (PER + 15) / 16; ++g) {
+    const uint32_t lo = 4096u * (uint32_t)g;
+    const rsrc_t rs = buffer_rsrc(srow + 1024 * g, bytes > lo ? bytes - lo : 0u);
+#pragma unroll
+    for (int m = 16 * g; m < min(PER, 16 * g + 16); ++m)
+      v[m] = __builtin_bit_cast(float, buffer_load4_nt(rs, 4u * (uint32_t)lane + 256u * (uint32_t)(m - 16 * g)));
   }
-  const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
-  const float* lp = srow + lane;
-#pragma unroll
-  for (int m = 0; m < PER; ++m) v[m] = m < kFullBlocks<PER> ? lp[64 * m] : srow[min(64 * m + lane, a.NB - 1)];
 }
 
 // Inclusive prefix sum over the wave's lanes; declared below.
@@ -192,23 +163,36 @@ __device__ __forceinline__ uint32_t emit(const uint32_t (&k)[N], const int32_t (
   return written;
 }
 
-constexpr int kSelectCand = 512;   // candidates per (row, head) the pruned search holds (8 per lane)
+constexpr int kSelectCand = 512;   // candidates per (row, head) the LDS holds (8 per lane)
+constexpr int kSelectStage = 256;  // results staged in LDS for one coalesced store when k fits
 
-// Search and emit over the ncand candidates compacted in LDS (page order:
-// score bits and page index), NC per lane: candidate 64 q + lane. Their keys
-// are made here, the tail page's the largest.
+// Per-wave LDS block of the candidates: score bits at [0, CAP), page indices
+// at [kIdxOff, kIdxOff + CAP), so one ds_write2st64 / ds_read2st64 moves both
+// (kIdxOff is a multiple of 64 dwords). Slots [CAP, CAP + 64) of each half
+// take the writes of lanes that hold no candidate (one per lane, so no two
+// lanes of a store meet). The staged results reuse the block's first dwords:
+// they are written only after every candidate is back in registers.
+constexpr int kCandPad = kSelectCand + 64;
+constexpr int kIdxOff = kCandPad;
+static_assert(kIdxOff % 64 == 0, "the index half must sit a whole number of 64-dword rows on");
+static_assert(kSelectStage <= kSelectCand, "the result stage must fit in the candidate block");
+
+// Search and emit over the ncand candidates compacted in LDS in page order,
+// NC per lane: candidate 64 q + lane. Their keys are made here, the tail
+// page's the largest. Slots past ncand hold stale values and are dropped.
 template <int NC>
-__device__ __forceinline__ uint32_t select_candidates(const uint32_t* ck, const uint16_t* ci, uint32_t ncand, int lane,
-                                                      int tail, uint32_t T0, int nbits, uint32_t keff, int32_t* sel,
+__device__ __forceinline__ uint32_t select_candidates(const uint32_t* cb, uint32_t ncand, int lane, int tail,
+                                                      uint32_t T0, int nbits, uint32_t keff, int32_t* sel,
                                                       int32_t* orow, uint32_t* hist) {
   uint32_t k2[NC];
   int32_t i2[NC];
 #pragma unroll
   for (int q = 0; q < NC; ++q) {
     const uint32_t c = 64 * q + lane;
-    const int32_t j = c < ncand ? (int32_t)ci[c] : -1;
-    k2[q] = c < ncand ? (j == tail ? 0xFFFFFFFFu : order_key_bits(ck[c])) : 0u;
-    i2[q] = j;
+    const uint32_t bits = cb[c];
+    const int32_t j = (int32_t)cb[kIdxOff + c];
+    k2[q] = c < ncand ? (j == tail ? 0xFFFFFFFFu : order_key_bits(bits)) : 0u;
+    i2[q] = c < ncand ? j : -1;
   }
   const uint32_t T = radix_threshold(k2, T0, nbits, keff, hist, lane);
   uint32_t gt = 0;
@@ -216,53 +200,46 @@ __device__ __forceinline__ uint32_t select_candidates(const uint32_t* ck, const 
   for (int q = 0; q < NC; ++q) gt += ballot_count(k2[q] > T);
   return emit(k2, i2, T, keff - gt, sel, orow);
 }
-constexpr int kSelectStage = 256;  // results staged in LDS for one coalesced store when k fits
 
-// Candidates per wave the LDS holds: every score for up to 1024 pages, 512
-// for longer rows (beyond, the search runs on the registers).
+// Scores per lane at which rows stop being searched on the registers directly
+// and candidates are compacted first (rows of up to 512 pages are searched in
+// registers).
+constexpr int kCompactPer = kSelectCand / 64;
+
+// Waves per SIMD the register budget is set for: eight hide the load
+// latency of rows up to 1024 pages; longer rows hold more scores per lane.
 template <int PER>
-constexpr int kCandCap = PER <= 16 ? 64 * PER : kSelectCand;
+constexpr int kSelectWaves = PER <= 16 ? 8 : (PER == 32 ? 4 : 2);
 
 template <int PER, bool TWO>
-__global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
-  constexpr int CAP = kCandCap<PER>;
-  __shared__ uint32_t cand_keys[kWaves][CAP];     // score bits
-  __shared__ uint16_t cand_idx[kWaves][CAP];      // page index (< 4096)
-  __shared__ int32_t sel_all[kWaves][kSelectStage];
+__global__ void __launch_bounds__(kThreads, kSelectWaves<PER>) k_select(SArgs a) {
+  constexpr int CAP = kSelectCand;
+  __shared__ uint32_t cand_all[kWaves][2 * kCandPad];
   __shared__ uint32_t hist_all[kWaves][64];   // radix threshold histogram
-  const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t wave = (int64_t)blockIdx.x * kWaves + wv;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
-  uint32_t* ck = cand_keys[wv];
-  uint16_t* ci = cand_idx[wv];
-  int32_t* sel = a.k <= kSelectStage ? sel_all[wv] : nullptr;
+  uint32_t* cb = cand_all[wv];
+  int32_t* sel = a.k <= kSelectStage ? reinterpret_cast<int32_t*>(cb) : nullptr;
   // Item = row * H + head. The grid stride nw is fixed, so (row, head) is
   // advanced by (nw / H, nw % H) with a carry instead of dividing per item
   // (a 64-bit division is a long scalar sequence).
   const int64_t step_r = nw / a.H;
   const int step_h = (int)(nw - step_r * a.H);
-  int64_t nr = wave / a.H;
-  int nh = (int)(wave - nr * a.H);
-  auto advance = [&]() {
-    nh += step_h;
-    nr += step_r;
-    if (nh >= a.H) {
-      nh -= a.H;
-      ++nr;
-    }
-  };
-  // the next item's scores are in flight while this one is selected
-  float nxt[PER];
-  if (wave < a.items) load_scores<PER>(a, nr, nh, lane, nxt);
+  int64_t r = wave / a.H;
+  int h = (int)(wave - r * a.H);
+  // The waves per SIMD hide the load latency; prefetching the next item's
+  // scores would cost PER more registers per lane and measured slower.
   for (int64_t item = wave; item < a.items; item += nw) {
+    // The lane index is opaque to the optimizer inside the loop: hoisted,
+    // each page index and offset derived from it (64 m + lane, ...) would
+    // hold a register of its own for the whole loop and push the kernel
+    // past the register budget.
+    int lane = (int)threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     float cur[PER];
-#pragma unroll
-    for (int m = 0; m < PER; ++m) cur[m] = nxt[m];
-    const int64_t r = nr;
-    const int h = nh;
-    advance();
-    if (item + nw < a.items) load_scores<PER>(a, nr, nh, lane, nxt);
+    const float* srow = a.bs + r * a.bs_row_stride + (int64_t)h * a.bs_head_stride;
+    load_scores<PER>(srow, a.NB, lane, cur);
     // the row's visible tokens, as the scorer masks them
     int lim;
     if (a.decode) {
@@ -277,105 +254,120 @@ __global__ void __launch_bounds__(kThreads) k_select(SArgs a) {
     }
     lim = clampi(lim, 0, a.max_seq_len);
     const int tail = lim > 0 ? (lim - 1) / a.P : -1;
+    int32_t* orow = a.out + r * a.out_row_stride + (int64_t)h * a.out_head_stride;
+    h += step_h;
+    r += step_r;
+    if (h >= a.H) {
+      h -= a.H;
+      ++r;
+    }
 
     // Per score, in floats: a dead page (-inf, or past the window: only the
-    // blocks that are not surely full can reach past NB) becomes -inf, each
-    // lane keeps its
-    // largest score (and, for k above 64, its second largest) and counts its
-    // live ones. Integer keys are made only for the candidates below.
+    // blocks that are not surely full can reach past NB) becomes -inf and
+    // each lane keeps its largest score (and, for k above 64, its second
+    // largest). Integer keys are made only for the candidates below.
     // The window width is opaque to the optimizer here: hoisted out of the
     // item loop, its lane mask would be spilled and reloaded for every item.
     int nb = a.NB;
     asm volatile("" : "+s"(nb));
     const float ninf = -__builtin_inff();
     float t1 = ninf, t2 = ninf;
-    uint32_t live_lane = 0;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
       const bool fin = __builtin_isfinite(cur[m]) && (m < kFullBlocks<PER> || 64 * m + lane < nb);
       cur[m] = fin ? cur[m] : ninf;
-      live_lane += fin ? 1u : 0u;
       if constexpr (TWO) t2 = __builtin_fmaxf(t2, __builtin_fminf(t1, cur[m]));
       t1 = __builtin_fmaxf(t1, cur[m]);
     }
-    const uint32_t live = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(live_lane), 63);
-    // the tail page is chosen whenever it is live
-    const int mt = tail >> 6, lt = tail & 63;
-    bool tail_live = false;
-    if (tail >= 0) {
+    // live pages: at least n1 (the lanes holding one), counted exactly only
+    // when that many might fall short of k
+    const uint32_t n1 = ballot_count(t1 != ninf);
+    uint32_t live = n1;
+    if (n1 < (uint32_t)a.k) {
+      live = 0;
 #pragma unroll
-      for (int m = 0; m < PER; ++m)
-        if (m == mt) tail_live = __ballot(lane == lt && cur[m] != ninf) != 0;
+      for (int m = 0; m < PER; ++m) live += ballot_count(cur[m] != ninf);
     }
     const uint32_t keff = min((uint32_t)a.k, live);
 
-    int32_t* orow = a.out + r * a.out_row_stride + (int64_t)h * a.out_head_stride;
     uint32_t written = 0;
     if (keff > 0) {
-      if (tail_live && keff == 1) {
-        // only the tail page
-        if (sel) { if (lane == 0) sel[0] = tail; } else if (lane == 0) orow[0] = tail;
-        written = 1;
-      } else {
-        // lower bound x of the k-th largest score: the smallest lane maximum
-        // when keff <= n1 lanes hold a live score (each holds one >= it),
-        // else the smallest second-largest when keff <= 2 n2, else none.
-        const uint32_t n1 = ballot_count(t1 != ninf);
-        float x = keff <= n1 ? wave_reduce_f<true>(t1 != ninf ? t1 : __builtin_inff()) : -__FLT_MAX__;
-        if constexpr (TWO) {
-          if (keff > n1) {
-            const uint32_t n2 = ballot_count(t2 != ninf);
-            if (keff <= 2 * n2) x = wave_reduce_f<true>(t2 != ninf ? t2 : __builtin_inff());
-          }
+      // lower bound x of the k-th largest key: the smallest lane maximum
+      // when keff <= n1 lanes hold a live score (each holds one >= it),
+      // else the smallest second-largest when keff <= 2 n2, else none
+      // (the key of the lowest finite score). Reduced as keys.
+      constexpr uint32_t kLowestKey = 0x00800001u;   // key of -FLT_MAX
+      const uint32_t k1 = t1 != ninf ? order_key(t1) : 0u;
+      uint32_t xk = keff <= n1 ? wave_min(k1 != 0u ? k1 : 0xFFFFFFFFu) : kLowestKey;
+      if constexpr (TWO) {
+        if (keff > n1) {
+          const uint32_t k2 = t2 != ninf ? order_key(t2) : 0u;
+          if (keff <= 2 * ballot_count(k2 != 0u)) xk = wave_min(k2 != 0u ? k2 : 0xFFFFFFFFu);
         }
-        // every candidate but the tail lies in [x, K]: the search only runs
-        // over the key bits below the prefix that x and K share
-        const uint32_t xk = order_key(x), K = order_key(wave_reduce_f<false>(t1));
-        const uint32_t diff = xk ^ K;
-        const int nbits = diff ? 32 - __builtin_clz(diff) : 0;
-        const uint32_t T0 = nbits == 32 ? 0u : (xk & ~((1u << nbits) - 1u));
-        // candidates (scores >= x, and the tail) compacted in page order
-        // (rows of up to 512 pages are searched in registers directly)
+      }
+      // every candidate but the tail lies in [x, K] (K the largest lane
+      // maximum; the tail's key is raised to the largest): the search only
+      // runs over the key bits below the prefix that x and K share
+      const uint32_t K = wave_max(k1);
+      const uint32_t diff = xk ^ K;
+      const int nbits = diff ? 32 - __builtin_clz(diff) : 0;
+      const uint32_t T0 = nbits == 32 ? 0u : (xk & ~((1u << nbits) - 1u));
+      const int mt = tail >> 6, lt = tail & 63;
+      bool done = false;
+      if (PER > kCompactPer) {
+        // Candidates compacted in page order: the scores >= x and, on the
+        // tail's lane, every live score, so the tail is among them whatever
+        // its score (its key is raised when they are read back; the others
+        // of that lane fall below T if they are below x).
+        const float x = __uint_as_float((xk & 0x80000000u) ? (xk & 0x7FFFFFFFu) : 0u - xk);
+        const float xl = (tail >= 0 && lane == lt) ? -__FLT_MAX__ : x;
+        // the last item's staged results (which share this block) are read
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         uint32_t ncand = 0;
+        const uint32_t spare = (uint32_t)(CAP + lane);
 #pragma unroll
-        for (int m = 0; m < (PER > kSelectCand / 64 ? PER : 0); ++m) {
-          bool c = cur[m] >= x;
-          if (m == mt) c = c || (tail_live && lane == lt);
+        for (int m = 0; m < (PER > kCompactPer ? PER : 0); ++m) {
+          const bool c = cur[m] >= xl;
           const uint64_t bc = __ballot(c);
-          const uint32_t at = ncand + lanes_below(bc);
-          if (c && (CAP >= 64 * PER || at < (uint32_t)CAP)) {
-            ck[at] = __float_as_uint(cur[m]);
-            ci[at] = (uint16_t)(64 * m + lane);
-          }
+          const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(bc >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bc, ncand));
+          uint32_t* cw = cb + min(c ? at : 0xFFFFFFFFu, spare);
+          cw[0] = __float_as_uint(cur[m]);
+          cw[kIdxOff] = (uint32_t)(64 * m + lane);
           ncand += __builtin_popcountll(bc);
         }
-        if (PER > kSelectCand / 64 && ncand <= (uint32_t)kSelectCand) {
+        if (ncand <= (uint32_t)CAP) {
+          done = true;
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           // the candidates back in registers, as few per lane as they need
           if (ncand <= 128)
-            written = select_candidates<2>(ck, ci, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+            written = select_candidates<2>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
           else if (ncand <= 256)
-            written = select_candidates<4>(ck, ci, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+            written = select_candidates<4>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
           else
-            written = select_candidates<8>(ck, ci, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
-        } else {
-          // short rows, or too many candidates: search the registers
-          uint32_t key[PER];
-          int32_t idx[PER];
-#pragma unroll
-          for (int m = 0; m < PER; ++m) {
-            idx[m] = 64 * m + lane;
-            key[m] = cur[m] == ninf ? 0u : order_key(cur[m]);
-            if (m == mt) key[m] = (tail_live && lane == lt) ? 0xFFFFFFFFu : key[m];
-          }
-          const uint32_t T = radix_threshold(key, T0, nbits, keff, hist_all[wv], lane);
-          uint32_t gt = 0;
-#pragma unroll
-          for (int m = 0; m < PER; ++m) gt += ballot_count(key[m] > T);
-          written = emit(key, idx, T, keff - gt, sel, orow);
+            written = select_candidates<8>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
         }
+      }
+      if (!done) {
+        // short rows, or too many candidates: search the registers (dead
+        // pages key 0, a live tail the largest key)
+        uint32_t key[PER];
+        int32_t idx[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          idx[m] = 64 * m + lane;
+          key[m] = cur[m] == ninf ? 0u : order_key(cur[m]);
+          if (m == mt) key[m] = (lane == lt && key[m] != 0u) ? 0xFFFFFFFFu : key[m];
+        }
+        const uint32_t T = radix_threshold(key, T0, nbits, keff, hist_all[wv], lane);
+        uint32_t gt = 0;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) gt += ballot_count(key[m] > T);
+        written = emit(key, idx, T, keff - gt, sel, orow);
       }
     }
     if (sel) {
