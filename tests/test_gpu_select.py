@@ -90,6 +90,30 @@ def test_decode_rows_and_strided_views(P):
     assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, 6))
 
 
+@pytest.mark.parametrize("NB", [300, 700, 1024, 2100])
+def test_live_pages_past_the_tail_and_tail_below_the_rest(NB):
+    # Distinct continuous scores, finite on every page: pages past a row's
+    # tail page are live (a finite score is what makes a page live), so the
+    # tail is not the last live page, and the tail's own score is pushed to
+    # the lowest on its row, so it is chosen only by the tail rule. Rows of
+    # 300 pages are searched on the registers, longer ones through the
+    # compacted candidates.
+    P, H = 128, 4
+    rng = np.random.default_rng(NB)
+    msl = NB * P
+    seq = [1, P + 5, msl // 3, msl // 2 + 17, msl - P, msl]
+    lim = topk.row_limits("decode", seq, msl)
+    s = rng.standard_normal((len(seq), H, NB)).astype(np.float32)
+    for r, L in enumerate(lim):
+        s[r, :, (int(L) - 1) // P] = -50.0
+    for k in (1, 16, 64):
+        say(f"decode select NB={NB} k={k}, live pages past the tail")
+        got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"),
+                              msl, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k)), k
+
+
 def test_many_items_per_wave_odd_head_count():
     # More (row, head) items than the grid has waves (the grid is capped at
     # 32 workgroups per CU), with 7 heads, which do not divide the grid
