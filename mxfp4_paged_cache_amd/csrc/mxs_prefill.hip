@@ -184,7 +184,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     // Write the staged scores of slot sl for the pages of its current 64-byte
     // segment (the one holding page j) from the item's first page on: lane
     // quarter q writes pages w + 4q .. w + 4q + 3, one 16-byte store when all
-    // four are this item's.
+    // four are this item's. The stores are non-temporal: held in L2 as usual,
+    // the 128-byte lines whose halves are written 16 pages apart went out to
+    // memory as about 10% more bytes than the scores (counted on the 4096-row
+    // prefill) and pushed the K pages the other workgroups were reading out
+    // of L2 (the chunked prefill fetched 1.7x more).
     auto flush_slot = [&](int sl, int j) {
       float* rp = reinterpret_cast<float*>(frow[sl]);
       const uint32_t ax = (uint32_t)(reinterpret_cast<uint64_t>(rp) >> 2);
@@ -192,11 +196,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
       const float* src = ring + sl * kPrefillStageStride;
       if (p0 >= j0 && p0 + 3 <= j) {
         const v4f v = {src[p0 & 15], src[(p0 + 1) & 15], src[(p0 + 2) & 15], src[(p0 + 3) & 15]};
-        *reinterpret_cast<v4f*>(rp + p0) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(rp + p0));
       } else {
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          if (p0 + x >= j0 && p0 + x <= j) rp[p0 + x] = src[(p0 + x) & 15];
+          if (p0 + x >= j0 && p0 + x <= j) __builtin_nontemporal_store(src[(p0 + x) & 15], rp + p0 + x);
       }
     };
 
