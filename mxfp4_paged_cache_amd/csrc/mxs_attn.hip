@@ -55,26 +55,35 @@ struct AttnUnit {
   int vsa[kUnit / 32], vsb[kUnit / 32];
 };
 
+// Loads go through buffer resources over the unit's bytes; a unit past the
+// row's context gets empty resources (its loads return zeros and read
+// nothing), so every unit's loads issue unconditionally and the waits on one
+// unit never cover the loads of the next (with the loads under a branch,
+// each unit waited for the next one's loads as well).
 __device__ __forceinline__ void load_attn_unit(AttnUnit& pg, const AArgs& a, int64_t page, int slot0, int hk,
-                                               int lane) {
+                                               int lane, bool live) {
   const int g = lane >> 4, i = lane & 15;
-  const uint8_t* kd = a.kd + page * a.kd_page_stride + (int64_t)hk * a.kd_head_stride + slot0 * 64;
-  const uint8_t* ks = a.ks + page * a.ks_page_stride + (int64_t)hk * a.ks_head_stride + slot0 * 4;
-  const uint8_t* vd = a.vd + page * a.vd_page_stride + (int64_t)hk * a.vd_head_stride + slot0 * 64;
-  const uint8_t* vs = a.vs + page * a.vs_page_stride + (int64_t)hk * a.vs_head_stride + slot0 * 4;
+  const rsrc_t kd = buffer_rsrc(a.kd + page * a.kd_page_stride + (int64_t)hk * a.kd_head_stride + slot0 * 64,
+                                live ? kUnit * 64 : 0);
+  const rsrc_t ks = buffer_rsrc(a.ks + page * a.ks_page_stride + (int64_t)hk * a.ks_head_stride + slot0 * 4,
+                                live ? kUnit * 4 : 0);
+  const rsrc_t vd = buffer_rsrc(a.vd + page * a.vd_page_stride + (int64_t)hk * a.vd_head_stride + slot0 * 64,
+                                live ? kUnit * 64 : 0);
+  const rsrc_t vs = buffer_rsrc(a.vs + page * a.vs_page_stride + (int64_t)hk * a.vs_head_stride + slot0 * 4,
+                                live ? kUnit * 4 : 0);
 #pragma unroll
   for (int t = 0; t < kUnit / 16; ++t) {
-    pg.kd[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(kd + (16 * t + i) * 64 + 16 * g));
-    pg.ks[t] = __builtin_nontemporal_load(ks + (16 * t + i) * 4 + g);
+    pg.kd[t] = buffer_load16_nt(kd, (uint32_t)((16 * t + i) * 64 + 16 * g));
+    pg.ks[t] = buffer_load1_nt(ks, (uint32_t)((16 * t + i) * 4 + g));
   }
   const int x = lane >> 2, pp = lane & 3;
 #pragma unroll
   for (int c = 0; c < kUnit / 32; ++c) {
     const int tok = 32 * c + x;
-    pg.va[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vd + tok * 64 + 16 * pp));
-    pg.vb[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vd + (tok + 16) * 64 + 16 * pp));
-    pg.vsa[c] = __builtin_nontemporal_load(vs + tok * 4 + pp);
-    pg.vsb[c] = __builtin_nontemporal_load(vs + (tok + 16) * 4 + pp);
+    pg.va[c] = buffer_load16_nt(vd, (uint32_t)(tok * 64 + 16 * pp));
+    pg.vb[c] = buffer_load16_nt(vd, (uint32_t)((tok + 16) * 64 + 16 * pp));
+    pg.vsa[c] = buffer_load1_nt(vs, (uint32_t)(tok * 4 + pp));
+    pg.vsb[c] = buffer_load1_nt(vs, (uint32_t)((tok + 16) * 4 + pp));
   }
 }
 
@@ -96,8 +105,10 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Three workgroups per CU (the LDS allows three): measured 5% faster than
+// two with the larger register budget.
 template <int QDT, int P>
-__global__ void __launch_bounds__(kThreads, 2) k_attn(AArgs a) {
+__global__ void __launch_bounds__(kThreads, 3) k_attn(AArgs a) {
   constexpr int TPP = kUnit / 16, CPP = kUnit / 32;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kAttnLds];
   __shared__ float mm[kWaves][16], ll[kWaves][16];
@@ -192,17 +203,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn(AArgs a) {
   // in flight while this one is processed
   {
     auto load = [&](AttnUnit& u, int j) {
-      const int t0 = j * kUnit;
-      load_attn_unit(u, a, btrow[t0 / P], t0 % P, hk, lane);
+      const bool live = j < nunits;
+      const int t0 = (live ? j : 0) * kUnit;
+      load_attn_unit(u, a, live ? btrow[t0 / P] : 0, t0 % P, hk, lane, live);
     };
     AttnUnit A, B;
     int j = wave;
-    if (j < nunits) load(A, j);
+    load(A, j);
     for (; j < nunits; j += 2 * kWaves) {
-      if (j + kWaves < nunits) load(B, j + kWaves);
+      load(B, j + kWaves);
       process(A, j);
       if (j + kWaves >= nunits) break;
-      if (j + 2 * kWaves < nunits) load(A, j + 2 * kWaves);
+      load(A, j + 2 * kWaves);
       process(B, j + kWaves);
     }
   }
