@@ -24,6 +24,10 @@ using namespace dev;
 // causal triangle (chunks past some rows' limits are cheap) costs every
 // workgroup the same.
 // ---------------------------------------------------------------------------
+// A float in global memory: the flush's row pointers come back from LDS as
+// plain integers, and as generic pointers their stores were flat stores,
+// whose completion the LDS waits of the next page also waited for.
+typedef __attribute__((address_space(1))) float gfloat;
 constexpr int kPrefillSlots = kWaves * kPrefillTiles * 16;   // query slots per work item
 constexpr int kWaveSlots = kPrefillTiles * 16;                // query slots per wave
 constexpr int kRingPages = 16;                                // block scores per slot in the LDS ring: 64 bytes
@@ -190,13 +194,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     // prefill) and pushed the K pages the other workgroups were reading out
     // of L2 (the chunked prefill fetched 1.7x more).
     auto flush_slot = [&](int sl, int j) {
-      float* rp = reinterpret_cast<float*>(frow[sl]);
+      gfloat* rp = reinterpret_cast<gfloat*>(frow[sl]);
       const uint32_t ax = (uint32_t)(reinterpret_cast<uint64_t>(rp) >> 2);
       const int p0 = j - (int)((ax + (uint32_t)j) & (kRingPages - 1)) + 4 * (lane & 3);
       const float* src = ring + sl * kPrefillStageStride;
       if (p0 >= j0 && p0 + 3 <= j) {
         const v4f v = {src[p0 & 15], src[(p0 + 1) & 15], src[(p0 + 2) & 15], src[(p0 + 3) & 15]};
-        __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(rp + p0));
+        __builtin_nontemporal_store(v, reinterpret_cast<__attribute__((address_space(1))) v4f*>(rp + p0));
       } else {
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -228,6 +232,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
           if (j + 1 - jid == 64) {
             jid += 64;
             ids = (jid + lane < jl) ? btrow[jid + lane] : 0;
+            // wait for the ids here: left to the page's readlane, the wait
+            // (whose counter also covers the block-score stores) went on
+            // every page, since the compiler cannot tell on which ones
+            // this load is in flight
+            asm volatile("" ::"v"(ids));
           }
           load_page(nx, __builtin_amdgcn_readlane(ids, j + 1 - jid));
         }
