@@ -344,10 +344,23 @@ __global__ void __launch_bounds__(kThreads, kSelectWaves<PER>) k_select(SArgs a)
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           // the candidates back in registers, as few per lane as they need
-          if (ncand <= 128)
+          // (every step of 64 has its own variant: the search and the emit
+          // cost per register held, and rounding 257 candidates up to eight
+          // per lane cost 5% of the top-64 selection)
+          if (ncand <= 64)
+            written = select_candidates<1>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+          else if (ncand <= 128)
             written = select_candidates<2>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+          else if (ncand <= 192)
+            written = select_candidates<3>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
           else if (ncand <= 256)
             written = select_candidates<4>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+          else if (ncand <= 320)
+            written = select_candidates<5>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+          else if (ncand <= 384)
+            written = select_candidates<6>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
+          else if (ncand <= 448)
+            written = select_candidates<7>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
           else
             written = select_candidates<8>(cb, ncand, lane, tail, T0, nbits, keff, sel, orow, hist_all[wv]);
         }
