@@ -114,6 +114,28 @@ def test_live_pages_past_the_tail_and_tail_below_the_rest(NB):
         assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k)), k
 
 
+@pytest.mark.parametrize("NB", [600, 1024, 1500])
+@pytest.mark.parametrize("k", [65, 128, 256, 257])
+def test_k_above_64_continuous_scores(NB, k):
+    # k above the 64 lanes: the lower bound comes from the lanes' second
+    # largest scores; up to 256 results are staged in LDS, 257 go straight to
+    # the output row. Continuous scores with dead pages in between, so the
+    # candidates are compacted (no ties to force the register search).
+    P, H = 128, 3
+    rng = np.random.default_rng(NB * 3 + k)
+    msl = NB * P
+    seq = [P * 3 + 1, msl // 2, msl - 5, msl]
+    lim = topk.row_limits("decode", seq, msl)
+    s = rng.standard_normal((len(seq), H, NB)).astype(np.float32)
+    s[rng.random(s.shape) < 0.05] = -np.inf
+    for r, L in enumerate(lim):
+        s[r, :, -(-int(L) // P):] = -np.inf
+    say(f"decode select NB={NB} k={k}, continuous scores")
+    got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
+
+
 def test_many_items_per_wave_odd_head_count():
     # More (row, head) items than the grid has waves (the grid is capped at
     # 32 workgroups per CU), with 7 heads, which do not divide the grid
