@@ -189,8 +189,11 @@ __device__ __forceinline__ uint32_t select_candidates(const uint32_t* cb, uint32
 #pragma unroll
   for (int q = 0; q < NC; ++q) {
     const uint32_t c = 64 * q + lane;
-    const uint32_t bits = cb[c];
-    const int32_t j = (int32_t)cb[kIdxOff + c];
+    uint32_t bits = cb[c];
+    int32_t j = (int32_t)cb[kIdxOff + c];
+    // every slot is read (stale ones are dropped here); without this the
+    // compiler turns each read into a branch around it
+    asm volatile("" : "+v"(bits), "+v"(j));
     k2[q] = c < ncand ? (j == tail ? 0xFFFFFFFFu : order_key_bits(bits)) : 0u;
     i2[q] = c < ncand ? j : -1;
   }
