@@ -85,9 +85,6 @@ __device__ __forceinline__ void load_scores(const float* srow, int NB, int lane,
   }
 }
 
-// Inclusive prefix sum over the wave's lanes; declared below.
-__device__ __forceinline__ uint32_t wave_scan(uint32_t x);
-
 // Inclusive prefix sum over the wave's lanes (DPP row shifts, then the
 // row-15 and row-31 broadcasts carry each row's total into the next rows).
 __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
@@ -101,8 +98,9 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
 }
 
 // The largest T with count(keys >= T) >= keff, over the bits below the first
-// 32 - nbits (T starts from those leading bits), found 6 bits per round: the keys that share T's
-// bits fixed so far are counted per next digit in the wave's LDS histogram
+// 32 - nbits (T starts from those leading bits), found 6 bits per round: the
+// keys that share T's bits fixed so far are counted per next digit in the
+// wave's LDS histogram
 // (64 bins, LDS atomics), and the digit is the largest whose count, with
 // every key already above, reaches keff. Lane l reads the bin of digit
 // 63 - l, so an inclusive scan over the lanes counts the keys at or above
