@@ -155,6 +155,16 @@ template <int N>
 __device__ __forceinline__ uint32_t emit(const uint32_t (&k)[N], const int32_t (&idx)[N], uint32_t T, uint32_t need_eq,
                                          int32_t* sel, int32_t* orow) {
   uint32_t written = 0, eq_seen = 0;
+  if (need_eq == 0u) {   // nothing taken at T (the search stopped on a bucket edge)
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const bool take = k[q] > T;
+      const uint64_t bt = __ballot(take);
+      if (take) (sel ? sel : orow)[written + lanes_below(bt)] = idx[q];
+      written += __builtin_popcountll(bt);
+    }
+    return written;
+  }
 #pragma unroll
   for (int q = 0; q < N; ++q) {
     const bool eq = k[q] == T;
@@ -282,7 +292,7 @@ __global__ void __launch_bounds__(kThreads, kSelectWaves<PER>) k_select(SArgs a)
     float t1 = ninf, t2 = ninf;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const bool fin = __builtin_isfinite(cur[m]) && (m < kFullBlocks<PER> || 64 * m + lane < nb);
+      const bool fin = __builtin_isfinite(cur[m]) && (m < kFullBlocks<PER> || lane < nb - 64 * m);
       cur[m] = fin ? cur[m] : ninf;
       if constexpr (TWO) t2 = __builtin_fmaxf(t2, __builtin_fminf(t1, cur[m]));
       t1 = __builtin_fmaxf(t1, cur[m]);
