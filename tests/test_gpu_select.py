@@ -136,6 +136,39 @@ def test_k_above_64_continuous_scores(NB, k):
     assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
 
 
+def test_seeded_sweep_of_shapes_and_score_kinds():
+    # 80 seeded cases: row lengths across every per-lane register count and
+    # the compaction limit, k from 1 to 400, and four kinds of scores:
+    # continuous, heavy ties, close values in one binade (long shared key
+    # prefixes), and continuous with -inf, NaN, +inf and -0.0 mixed in
+    rng = np.random.default_rng(2024)
+    for case in range(80):
+        NB = int(rng.choice([1, 5, 63, 64, 65, 200, 511, 512, 513, 700, 1000, 1024, 1025, 1500, 2048, 3000, 4096]))
+        k = int(rng.choice([1, 2, 7, 16, 31, 63, 64, 65, 100, 128, 200, 256, 257, 400]))
+        P = int(rng.choice([64, 128]))
+        H, R = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        kind = case % 4
+        msl = NB * P
+        seq = rng.integers(0, msl + 1, R)
+        lim = topk.row_limits("decode", seq, msl)
+        if kind == 0:
+            s = rng.standard_normal((R, H, NB)).astype(np.float32)
+        elif kind == 1:
+            s = rng.choice(np.linspace(-2, 2, 9).astype(np.float32), (R, H, NB))
+        elif kind == 2:
+            s = (rng.standard_normal((R, H, NB)) * 1e-3 + 5.0).astype(np.float32)
+        else:
+            s = rng.standard_normal((R, H, NB)).astype(np.float32)
+            s[rng.random(s.shape) < 0.3] = -np.inf
+            s[rng.random(s.shape) < 0.01] = np.float32(np.nan)
+            s[rng.random(s.shape) < 0.01] = np.float32(np.inf)
+            s[rng.random(s.shape) < 0.05] = np.float32(-0.0)
+        say(f"sweep case {case}: NB={NB} k={k} P={P} H={H} R={R} kind={kind}")
+        got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.from_numpy(seq.astype(np.int32)).cuda(), msl, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k)), case
+
+
 def test_many_items_per_wave_odd_head_count():
     # More (row, head) items than the grid has waves (the grid is capped at
     # 32 workgroups per CU), with 7 heads, which do not divide the grid
