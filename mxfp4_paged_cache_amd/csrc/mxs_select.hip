@@ -405,7 +405,9 @@ __global__ void __launch_bounds__(kThreads, kSelectWaves<PER>) k_select(SArgs a)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int p = lane; p < a.k; p += 64) orow[p] = (uint32_t)p < written ? sel[p] : -1;
+      // non-temporal: the ids are not read back here (231 -> 225 us for top-64
+      // over 4096 x 64 x 1024 block scores)
+      for (int p = lane; p < a.k; p += 64) __builtin_nontemporal_store((uint32_t)p < written ? sel[p] : -1, orow + p);
     } else {
       for (uint32_t p = written + lane; p < (uint32_t)a.k; p += 64) orow[p] = -1;
     }
