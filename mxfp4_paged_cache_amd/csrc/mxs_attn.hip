@@ -247,7 +247,8 @@ __global__ void __launch_bounds__(kThreads, 3) k_attn(AArgs a) {
       }
       val = O / L;
     }
-    a.out[(int64_t)r * a.out_row_stride + (int64_t)(hk * a.G + h) * a.out_head_stride + d] = (uint16_t)bf16_bits(val);
+    __builtin_nontemporal_store((uint16_t)bf16_bits(val),
+                                a.out + (int64_t)r * a.out_row_stride + (int64_t)(hk * a.G + h) * a.out_head_stride + d);
   }
 }
 

@@ -241,12 +241,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode(KArgs a) {
   }
   // Block scores leave LDS as one contiguous run of (j1 - j0) floats per head:
   // consecutive lanes write consecutive pages, so every store instruction
-  // covers whole cache lines instead of 64 scattered 4-byte words.
+  // covers whole cache lines instead of 64 scattered 4-byte words. The stores
+  // are non-temporal (nothing here reads them back; 1% on the decode workload).
   const int npg = j1 - j0;
   const int nh = min(kDecodeHeads, a.H - hg * kDecodeHeads);
   for (int idx = lane; idx < nh * npg; idx += 64) {
     const int h = idx / npg, p = idx - h * npg;
-    bs_row[(int64_t)(hg * kDecodeHeads + h) * a.bs_head_stride + j0 + p] = stage[h * kDecodeStageStride + p];
+    __builtin_nontemporal_store(stage[h * kDecodeStageStride + p],
+                                bs_row + (int64_t)(hg * kDecodeHeads + h) * a.bs_head_stride + j0 + p);
   }
 }
 
