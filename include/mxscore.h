@@ -147,7 +147,7 @@ typedef struct mxs_batch {
   int32_t batch;               /* >= 0 */
   int32_t total_rows;          /* prefill/logits: cu_seqlens_q[batch]; decode: ignored */
   int32_t max_query_len;       /* prefill/logits: >= every request's q_len; decode: ignored */
-  int32_t max_seq_len;         /* output window in tokens, >= 0 */
+  int32_t max_seq_len;         /* output window in tokens, 0 .. 2^31 - 256 */
 } mxs_batch;
 
 /* Launch plan: a pure function of host integers (mode, shapes, page size,
@@ -312,7 +312,8 @@ typedef struct mxs_kvcache {
  * read as MXFP4 by a paged decode attention, one row per (token, kv head);
  * the K/V format as above). For row r and query head h (kv head
  * hk = h / G, G = q->num_heads / kv->num_kv_heads, 1 <= G <= 16) over the
- * row's live tokens t < min(context_lens[r], max_context):
+ * row's live tokens t < min(context_lens[r], max_context) (max_context
+ * 0 .. 2^31 - 256):
  *     s_t = scale * (Q_hat[r, h] . K[t]),  out[r, h] = sum_t softmax(s)_t V[t]
  * Q_hat is the query rounded as the scorers round it (bf16 -> e4m3, nearest
  * even, saturating, unit scale; e4m3 used as stored). Token t of row r is in

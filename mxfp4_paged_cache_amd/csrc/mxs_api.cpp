@@ -184,6 +184,8 @@ int mxs_select_pages(int32_t mode, const mxs_batch* bt, int32_t num_heads, int32
   if (num_heads < 1) return fail(MXS_EINVAL, "num_heads must be >= 1, got %d", num_heads);
   if (k < 0) return fail(MXS_EINVAL, "k must be >= 0, got %d", k);
   if (bt->batch < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  if (bt->max_seq_len > mxs::kMaxSeqLen)
+    return fail(MXS_EINVAL, "max_seq_len %d is above the limit %d", bt->max_seq_len, mxs::kMaxSeqLen);
   const bool decode = mode == MXS_MODE_DECODE;
   if (!decode && bt->total_rows < 0) return fail(MXS_EINVAL, "total_rows must be >= 0");
   const int64_t rows = decode ? bt->batch : bt->total_rows;
@@ -253,6 +255,8 @@ int mxs_check_metadata(int32_t mode, const mxs_kcache* k, const mxs_batch* bt, i
   const bool fp8 = k->k_dtype == MXS_K_E4M3;
   const int32_t B = bt->batch, P = k->page_size;
   if (B < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  if (bt->max_seq_len > mxs::kMaxSeqLen)
+    return fail(MXS_EINVAL, "max_seq_len %d is above the limit %d", bt->max_seq_len, mxs::kMaxSeqLen);
   if (B == 0) return MXS_OK;
   if (!bt->block_table || !bt->seq_lens || (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens)))
     return fail(MXS_EINVAL, "metadata pointers must not be NULL");
@@ -354,6 +358,8 @@ int mxs_attn_decode(const mxs_query* q, const mxs_kvcache* kv, const int32_t* bl
   const int32_t G = q->num_heads / kv->num_kv_heads;
   if (G > 16) return fail(MXS_EUNSUPPORTED, "at most 16 query heads per kv head, got %d", G);
   if (num_rows < 0 || max_context < 0) return fail(MXS_EINVAL, "num_rows and max_context must be >= 0");
+  if (max_context > mxs::kMaxSeqLen)
+    return fail(MXS_EINVAL, "max_context %d is above the limit %d", max_context, mxs::kMaxSeqLen);
   if (!(std::isfinite(scale) && scale > 0.0f)) return fail(MXS_EINVAL, "scale must be finite and > 0");
   if (num_rows == 0) return MXS_OK;
   const int P = kv->page_size, Hkv = kv->num_kv_heads;
@@ -459,6 +465,8 @@ int mxs_plan_make_for(int32_t mode, int32_t q_dtype, int32_t k_dtype, int32_t pa
   if (batch < 0 || max_seq_len < 0 || (mode != MXS_MODE_DECODE && max_query_len < 0))
     return fail(MXS_EINVAL, "negative batch (%d), max_query_len (%d) or max_seq_len (%d)", batch, max_query_len,
                 max_seq_len);
+  if (max_seq_len > mxs::kMaxSeqLen)
+    return fail(MXS_EINVAL, "max_seq_len %d is above the limit %d", max_seq_len, mxs::kMaxSeqLen);
   if (parallel_unit_num < 0) return fail(MXS_EINVAL, "parallel_unit_num must be >= 0");
   if (num_cus < 1 || wg_per_cu < 1) return fail(MXS_EINVAL, "device description must be positive");
   if (mode == MXS_MODE_LOGITS && !want_logits) return fail(MXS_EINVAL, "logits mode needs logits");
@@ -649,6 +657,8 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
   if (check_k_dtype(k->k_dtype)) return MXS_EDTYPE;
   if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return fail(MXS_EINVAL, "sm_scale must be finite and > 0");
   if (bt->batch < 0 || bt->max_seq_len < 0) return fail(MXS_EINVAL, "batch and max_seq_len must be >= 0");
+  if (bt->max_seq_len > mxs::kMaxSeqLen)
+    return fail(MXS_EINVAL, "max_seq_len %d is above the limit %d", bt->max_seq_len, mxs::kMaxSeqLen);
   const bool decode = mode == MXS_MODE_DECODE;
   if (!decode && (bt->total_rows < 0 || bt->max_query_len < 0))
     return fail(MXS_EINVAL, "total_rows and max_query_len must be >= 0");

@@ -263,6 +263,15 @@ __device__ __forceinline__ void stage_store(const PageStage<KDT, P>& st, uint8_t
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Tokens that query row i (0-based within its request) sees before the
+// output window clips them: min(seq_len, prefix_len + i + 1), taken in 64-bit
+// so that no prefix_len, however large, wraps the sum (aiter #7061,
+// "Kernels": the causal limit of a prefill row).
+__device__ __forceinline__ int causal_limit(int seq, int pre, int64_t i) {
+  const int64_t c = (int64_t)pre + i + 1;
+  return c < (int64_t)seq ? (int)c : seq;
+}
+
 // Raw buffer resource over [base, base + bytes) (no stride, no swizzle).
 // A buffer load at an offset at or past `bytes` returns zeros without a
 // memory request, so bytes = 0 turns every load through the resource into a

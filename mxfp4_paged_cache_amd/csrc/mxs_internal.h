@@ -19,6 +19,9 @@ enum KernelId : int32_t {
 };
 
 constexpr int kWaves = 4;           // waves per workgroup, every kernel
+// Longest output window / context in tokens: page-rounded token indices
+// (ceil(max_seq_len / P) * P) then stay within int32.
+constexpr int32_t kMaxSeqLen = INT32_MAX - 255;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefillTiles = 8;    // 16-slot query tiles per wave (block-score kernel)
 constexpr int kLogitsTiles = 1;     // 16-slot query tiles per wave (logits kernel)

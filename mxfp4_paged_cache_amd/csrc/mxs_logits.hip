@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     if (sbeg >= nslots) continue;   // uniform over the workgroup
     const int seq = a.seq[b], pre = a.decode_rows ? seq - 1 : a.prefix[b];
     const int64_t slast = min(sbeg + (int64_t)kLogitsSlots, nslots) - 1;
-    const int item_lim = clampi(min(seq, pre + (int)(slast / a.H) + 1), 0, W);
+    const int item_lim = clampi(causal_limit(seq, pre, slast / a.H), 0, W);
 
     // the wave's tile: slots wbeg .. wbeg + 15; slot wbeg is (row r0, head h0)
     const int64_t wbeg = sbeg + (int64_t)wave * 16;
@@ -82,15 +82,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     const bool valid = wbeg + i < nslots;
     const uint32_t hi_ = (uint32_t)h0 + (uint32_t)(valid ? i : 0);
     const int r = r0 + (int)(hi_ / (uint32_t)a.H), h = (int)(hi_ % (uint32_t)a.H);
-    const int lim = valid ? clampi(min(seq, pre + r + 1), 0, W) : 0;
+    const int lim = valid ? clampi(causal_limit(seq, pre, r), 0, W) : 0;
     const v8i qt =
         load_q_tile_masked<QDT>(a.q + ((int64_t)row0 + r) * a.q_row_stride + (int64_t)h * a.q_head_stride, g, valid);
     float* bsp = (WANT_BS && valid) ? a.bs + ((int64_t)row0 + r) * a.bs_row_stride + (int64_t)h * a.bs_head_stride
                                     : nullptr;
     // limits of the wave's first and last slot (rows only grow along the slots)
     const int64_t wlast = min(wbeg + 15, nslots - 1);
-    const int wave_min_lim = wave_live ? clampi(min(seq, pre + r0 + 1), 0, W) : 0;
-    const int wave_max_lim = wave_live ? clampi(min(seq, pre + (int)(wlast / a.H) + 1), 0, W) : 0;
+    const int wave_min_lim = wave_live ? clampi(causal_limit(seq, pre, r0), 0, W) : 0;
+    const int wave_max_lim = wave_live ? clampi(causal_limit(seq, pre, wlast / a.H), 0, W) : 0;
     // logits rows this lane writes out: slots wbeg + 2 q + wrow
     float* orow[8];
 #pragma unroll

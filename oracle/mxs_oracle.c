@@ -278,8 +278,8 @@ int mxo_score_ex(const mxo_args* a, float* logits, float* blocks, double* mags, 
       limit = a->seq_lens[b];
     } else {
       int i = r - a->cu_seqlens_q[b];
-      int causal = a->prefix_lens[b] + i + 1;
-      limit = a->seq_lens[b] < causal ? a->seq_lens[b] : causal;
+      int64_t causal = (int64_t)a->prefix_lens[b] + i + 1;   /* integers: no int32 wrap */
+      limit = a->seq_lens[b] < causal ? a->seq_lens[b] : (int)causal;
     }
     if (limit > W) limit = W;   /* the output window ends at max_seq_len */
     if (limit < 0) limit = 0;

@@ -90,6 +90,8 @@ CASES = [
     ("null scale view (MXFP4)", lambda q, k, b, bs, lg: setattr(k, "scale", None), mx.MXS_EINVAL),
     # an fp8 cache needs 128 bytes per token: the 8704-byte MXFP4 page stride is too narrow
     ("narrow fp8 data view", lambda q, k, b, bs, lg: setattr(k, "k_dtype", mx.MXS_K_E4M3), mx.MXS_ELAYOUT),
+    # page-rounded token indices must stay within int32
+    ("window above 2^31 - 256", lambda q, k, b, bs, lg: setattr(b, "max_seq_len", 2**31 - 255), mx.MXS_EINVAL),
 ]
 
 
@@ -227,6 +229,8 @@ def test_plan_rejections(L):
     assert plan_for(L, mx.MXS_MODE_DECODE, kd=7)[0] == mx.MXS_EDTYPE
     assert plan_for(L, mx.MXS_MODE_DECODE, H=0)[0] == mx.MXS_EINVAL
     assert plan_for(L, mx.MXS_MODE_LOGITS, lg=0)[0] == mx.MXS_EINVAL
+    assert plan_for(L, mx.MXS_MODE_DECODE, msl=2**31 - 255)[0] == mx.MXS_EINVAL
+    assert plan_for(L, mx.MXS_MODE_DECODE, msl=2**31 - 256)[0] == mx.MXS_OK     # the largest window planned
 
 
 def test_check_metadata_rejections_before_any_copy(L):
@@ -243,6 +247,10 @@ def test_check_metadata_rejections_before_any_copy(L):
     nulls.seq_lens = None
     assert L.mxs_check_metadata(mx.MXS_MODE_DECODE, ctypes.byref(k), ctypes.byref(nulls), 0, None) == mx.MXS_EINVAL
     assert b"NULL" in L.mxs_last_error()
+    wide = mx.Batch.from_buffer_copy(bytes(b))
+    wide.max_seq_len = 2**31 - 255
+    assert L.mxs_check_metadata(mx.MXS_MODE_PREFILL, ctypes.byref(k), ctypes.byref(wide), 0, None) == mx.MXS_EINVAL
+    assert b"limit" in L.mxs_last_error()
 
 
 def test_select_pages_rejections_before_device_work(L):
@@ -260,6 +268,8 @@ def test_select_pages_rejections_before_device_work(L):
     wide = mx.Batch.from_buffer_copy(bytes(b))
     wide.max_seq_len = 128 * 4097
     assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4, rs=64 * 4097, hs=4097) == mx.MXS_EUNSUPPORTED
+    wide.max_seq_len = 2**31 - 255
+    assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4) == mx.MXS_EINVAL
 
 
 def test_write_pages_rejections_before_device_work(L):
@@ -344,6 +354,7 @@ def test_attn_decode_rejections_before_device_work(L):
         ("narrow output rows", lambda q, kv: None, {"ors": 128}, mx.MXS_ELAYOUT),
         ("null output", lambda q, kv: None, {"out": None}, mx.MXS_EINVAL),
         ("misaligned query", lambda q, kv: setattr(q, "ptr", FAKE + 8), {}, mx.MXS_ELAYOUT),
+        ("context above 2^31 - 256", lambda q, kv: None, {"maxc": 2**31 - 255, "btw": 2**24}, mx.MXS_EINVAL),
     ]
     for name, mutate, kw, code in cases:
         q, kv = attn_args()

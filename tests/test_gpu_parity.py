@@ -90,6 +90,17 @@ def test_prefill_many_rows_ragged_pages(lg):
 
 
 @LOGITS
+def test_prefix_near_int32_max(lg):
+    # prefix_len + i + 1 passes 2^31 - 1 from the second row of the first
+    # request on; the limit min(seq_len, prefix_len + i + 1) is over the
+    # integers, so those rows see their whole sequence (an int32 sum wraps
+    # negative and masks them out)
+    wl = W.Workload("prefill_huge_prefix", "prefill", H=16, page_size=64, q_lens=[3, 2], prefix_lens=[2**31 - 2, 5],
+                    seq_lens=[70, 7], want_logits=lg, max_seq_len=80)
+    check_case(wl, seed=21)
+
+
+@LOGITS
 def test_prefill_e4m3_query_long_rows(lg):
     wl = W.Workload("prefill_e4m3", "prefill", H=64, page_size=128, q_lens=[40], prefix_lens=[2000],
                     seq_lens=[2040], q_dtype="e4m3", want_logits=lg)

@@ -54,6 +54,25 @@ def test_prefill_rows_match_oracle(NB, k):
     assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
 
 
+def test_prefix_near_int32_max():
+    # rows whose prefix_len + i + 1 passes 2^31 - 1: their limit is seq_len,
+    # so the tail page is the sequence's last
+    P, NB, k = 64, 8, 3
+    rng = np.random.default_rng(77)
+    q_lens, prefix, seq = [3, 2], [2**31 - 2, 10], [450, 12]
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    msl = NB * P
+    lim = topk.row_limits("prefill", seq, msl, cu, prefix)
+    assert lim.tolist() == [450, 450, 450, 11, 12]
+    s = synthetic_scores(rng, lim, 3, P, NB)
+    say(f"prefill select with prefix 2^31 - 2, NB={NB} k={k}")
+    got = mx.select_pages(torch.from_numpy(s).cuda(), k, torch.tensor(seq, dtype=torch.int32, device="cuda"), msl, P,
+                          cu_seqlens_q=torch.from_numpy(cu).cuda(),
+                          prefix_lens=torch.tensor(prefix, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), topk.select_pages(s, lim, P, k))
+
+
 @pytest.mark.parametrize("NB,k", [(2100, 300), (4096, 600)])
 def test_large_k(NB, k):
     # k above the 256 results staged in LDS: ids go straight to the output

@@ -239,6 +239,19 @@ def test_causal_prefix_example(oracle_lib):
     assert live.tolist() == [[True, True, True, False], [True, True, True, True]]
 
 
+def test_causal_limit_with_prefix_near_int32_max(oracle_lib):
+    # The limit min(seq_len, prefix_len + i + 1) is a statement about
+    # integers: with prefix 2^31 - 2 the sum passes 2^31 - 1 from the second
+    # row on, and every row still sees its whole sequence. Catches: the sum
+    # taken in int32 (wraps negative and masks the row out).
+    rng = np.random.default_rng(4)
+    c = random_case(rng, B=1, H=2, page_size=64, q_lens=[3], prefix_lens=[2**31 - 2], seq_lens=[70])
+    r = run_c(c, page_size=64, max_seq_len=80)
+    live = np.isfinite(r.logits)
+    assert live[:, :, :70].all() and not live[:, :, 70:].any()
+    assert np.array_equal(live[:, 0, :], _live_mask(c, "prefill", 80))
+
+
 # ------------------------------------------------------------------ closed forms
 
 def test_e4m3_exact_window_is_119_to_133(oracle_lib):
