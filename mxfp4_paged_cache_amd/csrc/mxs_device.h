@@ -263,13 +263,12 @@ __device__ __forceinline__ void stage_store(const PageStage<KDT, P>& st, uint8_t
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Tokens that query row i (0-based within its request) sees before the
-// output window clips them: min(seq_len, prefix_len + i + 1), taken in 64-bit
-// so that no prefix_len, however large, wraps the sum (aiter #7061,
-// "Kernels": the causal limit of a prefill row).
-__device__ __forceinline__ int causal_limit(int seq, int pre, int64_t i) {
-  const int64_t c = (int64_t)pre + i + 1;
-  return c < (int64_t)seq ? (int)c : seq;
+// Tokens that query row i >= 0 (within its request) sees before the output
+// window clips them: min(seq_len, prefix_len + i + 1) (aiter #7061,
+// "Kernels": the causal limit of a prefill row). The sum is formed only when
+// it is below seq_len, so no prefix_len, however large, wraps it.
+__device__ __forceinline__ int causal_limit(int seq, int pre, int i) {
+  return pre < seq - i ? pre + i + 1 : seq;
 }
 
 // Raw buffer resource over [base, base + bytes) (no stride, no swizzle).

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     if (sbeg >= nslots) continue;   // uniform over the workgroup
     const int seq = a.seq[b], pre = a.decode_rows ? seq - 1 : a.prefix[b];
     const int64_t slast = min(sbeg + (int64_t)kLogitsSlots, nslots) - 1;
-    const int item_lim = clampi(causal_limit(seq, pre, slast / a.H), 0, W);
+    const int item_lim = clampi(causal_limit(seq, pre, (int)(slast / a.H)), 0, W);
 
     // the wave's tile: slots wbeg .. wbeg + 15; slot wbeg is (row r0, head h0)
     const int64_t wbeg = sbeg + (int64_t)wave * 16;
@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_logits(KArgs a) {
     // limits of the wave's first and last slot (rows only grow along the slots)
     const int64_t wlast = min(wbeg + 15, nslots - 1);
     const int wave_min_lim = wave_live ? clampi(causal_limit(seq, pre, r0), 0, W) : 0;
-    const int wave_max_lim = wave_live ? clampi(causal_limit(seq, pre, wlast / a.H), 0, W) : 0;
+    const int wave_max_lim = wave_live ? clampi(causal_limit(seq, pre, (int)(wlast / a.H)), 0, W) : 0;
     // logits rows this lane writes out: slots wbeg + 2 q + wrow
     float* orow[8];
 #pragma unroll

@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     if (sbeg >= nslots) continue;   // uniform over the workgroup
     const int seq = a.seq[b], pre = a.prefix[b];
     const int64_t slast = min(sbeg + (int64_t)kPrefillSlots, nslots) - 1;
-    const int item_lim = clampi(causal_limit(seq, pre, slast / a.H), 0, a.max_seq_len);
+    const int item_lim = clampi(causal_limit(seq, pre, (int)(slast / a.H)), 0, a.max_seq_len);
 
     // this lane's query slots
     v8i qt[NQ];
@@ -151,7 +151,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill(KArgs a) {
     }
     // smallest limit among this wave's slots: the limit of its first slot
     const int64_t wfirst = sbeg + (int64_t)wave * NQ * 16;
-    const int wave_min_lim = wfirst < nslots ? clampi(causal_limit(seq, pre, wfirst / a.H), 0, a.max_seq_len) : 0;
+    const int wave_min_lim =
+        wfirst < nslots ? clampi(causal_limit(seq, pre, (int)(wfirst / a.H)), 0, a.max_seq_len) : 0;
 
     const int j0 = pc * a.pages_per_item;
     const int j1 = min(j0 + a.pages_per_item, a.NB);

@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(kThreads, kSelectWaves<PER>) k_select(SArgs a)
         const int mid = (lo + hi + 1) >> 1;
         if (a.cu[mid] <= r) lo = mid; else hi = mid - 1;
       }
-      lim = causal_limit(a.seq[lo], a.prefix[lo], (int64_t)r - a.cu[lo]);
+      lim = causal_limit(a.seq[lo], a.prefix[lo], (int)(r - a.cu[lo]));
     }
     lim = clampi(lim, 0, a.max_seq_len);
     const int tail = lim > 0 ? (lim - 1) / a.P : -1;
