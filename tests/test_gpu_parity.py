@@ -128,6 +128,68 @@ def test_wide_scale_bytes_per_token(lg):
     check_case(wl, seed=15, min_exact=0.999, out_bs=3, out_lg=122)
 
 
+def _sweep_workload(rng, n):
+    """One seeded shape: mode, heads, page size, query dtype, ragged and empty
+    requests, limits clipped by seq_len or by the causal diagonal, a window
+    past the longest sequence, both scale-byte ranges, table fills, layouts."""
+    mode = ("prefill", "prefill", "logits", "decode")[int(rng.integers(4))]
+    H = int(rng.choice([1, 2, 5, 16, 17, 24, 64]))
+    P = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 6))
+    if mode == "decode":
+        q_lens, prefix = [1] * B, [0] * B
+        seq = [int(rng.integers(0, 1200)) for _ in range(B)]
+    else:
+        q_lens = [int(rng.integers(0, 41)) for _ in range(B)]
+        prefix = [int(rng.integers(0, 700)) for _ in range(B)]
+        seq = []
+        for p_, q_ in zip(prefix, q_lens):
+            kind = int(rng.integers(4))
+            if kind == 2:      # seq_len below prefix + q_len: the last rows see seq_len tokens
+                seq.append(max(0, p_ + q_ - int(rng.integers(1, 60))))
+            elif kind == 3:    # seq_len past the diagonal of the last row
+                seq.append(p_ + q_ + int(rng.integers(1, 90)))
+            else:
+                seq.append(p_ + q_)
+    window = max(seq + [1]) + int(rng.integers(0, 3 * P))
+    wide = bool(rng.random() < 0.25)
+    return W.Workload(f"sweep{n}", mode, H=H, page_size=P, q_lens=q_lens, prefix_lens=prefix, seq_lens=seq,
+                      q_dtype=str(rng.choice(["bf16", "e4m3"])), scale_lo=100 if wide else 122,
+                      scale_hi=150 if wide else 127, want_logits=mode == "logits" or bool(rng.random() < 0.5),
+                      max_seq_len=window, table_fill=str(rng.choice(["pad", "perm"])),
+                      layout=str(rng.choice(["split", "region"]))), wide
+
+
+def test_seeded_sweep_of_shapes():
+    # 48 seeded shapes through the C ABI against the oracle. Masks, -inf
+    # patterns and layouts compare exactly; every finite value lies within
+    # 2^-10 * sm_scale * M, and those outside 2^-20 relative stay under 0.1%
+    # of a case's finite values (1% with bytes 100..150 per 32-element block,
+    # at least 4 per case); argmax positions that differ must be near ties
+    # and stay under 1% of the (row, head) pairs.
+    rng = np.random.default_rng(2026)
+    for n in range(48):
+        wl, wide = _sweep_workload(rng, n)
+        say(f"case sweep{n}: mode={wl.mode} H={wl.H} P={wl.page_size} q={wl.q_dtype} B={wl.B} q_lens={wl.q_lens} "
+            f"prefix={wl.prefix_lens} seq={wl.seq_lens} window={wl.window} wide={wide} logits={wl.want_logits} "
+            f"fill={wl.table_fill} layout={wl.layout}")
+        host = W.make_inputs(wl, 3000 + n, "cpu")
+        dev = gpu_inputs(host)
+        bs, lg = run_gpu(dev)
+        torch.cuda.synchronize()
+        ref = oracle_run(host, want_logits=True, want_blocks=True)
+        frac = 0.01 if wide else 0.001
+        ceil = lambda ref_: max(4, int(frac * np.isfinite(ref_).sum()))
+        if bs is not None:
+            compare(bs.cpu().numpy(), ref.blocks, ref.block_mags, S, what=f"sweep{n} block scores",
+                    min_exact=0.5 if wide else 0.99, max_outside=ceil(ref.blocks))
+            compare_argmax(bs.cpu().numpy(), ref.blocks, ref.block_mags, S, f"sweep{n} block scores",
+                           max_diff=max(1, wl.T * wl.H // 100))
+        if lg is not None:
+            compare(lg.cpu().numpy(), ref.logits, ref.mags, S, what=f"sweep{n} logits",
+                    min_exact=0.5 if wide else 0.99, max_outside=ceil(ref.logits))
+
+
 def test_logits_shared_region_small():
     # two-slot shared region, slot 1 scored, 64-token pages, padded table rows,
     # window not a multiple of the page size
