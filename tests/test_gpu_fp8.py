@@ -15,7 +15,7 @@ from mxfp4_paged_cache_amd import workloads as W
 from oracle import writer
 from tests.gpu_helpers import (compare, compare_argmax, gpu_inputs, oracle_run, run_gpu, say)
 from tests.test_gpu_write import make_keys
-from tests.test_gpu_parity import _sample_rows
+from tests.test_gpu_parity import _sample_rows, _sweep_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,34 @@ def check_case(wl: W.Workload, *, seed=0):
     if lg is not None:
         compare(lg.cpu().numpy(), ref.logits, ref.mags, S, what="logits", **FP8)
     return host, dev, bs, lg
+
+
+def test_fp8_seeded_sweep_of_shapes():
+    # 24 seeded shapes of the MXFP4 sweep on an fp8 cache (NaN bytes past every
+    # request's end): masks and layouts compare exactly, values under the fp8
+    # rule above (in a case of a hundred values all may miss 2^-20 relative:
+    # the bound on every value and the 99th percentile carry the check),
+    # differing argmax positions near ties under 1% of the (row, head) pairs
+    import dataclasses
+    rule = dict(FP8, max_outside=1.0)
+    rng = np.random.default_rng(2027)
+    for n in range(24):
+        wl, _ = _sweep_workload(rng, n)
+        wl = dataclasses.replace(wl, name=f"fp8sweep{n}", k_dtype="e4m3", scale_lo=127, scale_hi=127)
+        say(f"case fp8sweep{n}: mode={wl.mode} H={wl.H} P={wl.page_size} q={wl.q_dtype} q_lens={wl.q_lens} "
+            f"prefix={wl.prefix_lens} seq={wl.seq_lens} window={wl.window} logits={wl.want_logits}")
+        host = W.make_inputs(wl, 4000 + n, "cpu")
+        poison_tails(host)
+        dev = gpu_inputs(host)
+        bs, lg = run_gpu(dev)
+        torch.cuda.synchronize()
+        ref = oracle_run(host, want_logits=True, want_blocks=True)
+        if bs is not None:
+            compare(bs.cpu().numpy(), ref.blocks, ref.block_mags, S, what=f"fp8sweep{n} block scores", **rule)
+            compare_argmax(bs.cpu().numpy(), ref.blocks, ref.block_mags, S, f"fp8sweep{n} block scores",
+                           max_diff=max(1, wl.T * wl.H // 100))
+        if lg is not None:
+            compare(lg.cpu().numpy(), ref.logits, ref.mags, S, what=f"fp8sweep{n} logits", **rule)
 
 
 @pytest.mark.parametrize("P", [64, 128])
