@@ -122,6 +122,31 @@ def test_attn_matches_oracle(P, q_dtype, Hkv, G):
     assert np.all(got[0] == 0.0)                         # a row with no token gives zeros
 
 
+def test_attn_seeded_sweep_of_shapes():
+    # 24 seeded shapes: rows, kv heads, query heads per kv head (1..16), page
+    # size, query dtype, contexts from 0 to past a page boundary and long ones,
+    # both scale-byte ranges, and max_context below the longest context
+    rng = np.random.default_rng(2028)
+    for n in range(24):
+        P = int(rng.choice([64, 128]))
+        R = int(rng.integers(1, 41))
+        Hkv = int(rng.integers(1, 5))
+        G = int(rng.choice([1, 2, 3, 5, 8, 16]))
+        edges = [0, 1, P - 1, P, P + 1]
+        ctx = [int(rng.choice(edges)) if rng.random() < 0.3 else int(rng.integers(0, 1500)) for _ in range(R)]
+        wide = bool(rng.random() < 0.25)
+        q_dtype = str(rng.choice(["bf16", "e4m3"]))
+        clamp = bool(rng.random() < 0.25) and max(ctx) > 1
+        mc = int(rng.integers(1, max(ctx))) if clamp else None
+        say(f"attn sweep{n}: P={P} R={R} Hkv={Hkv} G={G} q={q_dtype} wide={wide} max_context={mc} ctx={ctx}")
+        c = make_case(5000 + n, R=R, Hkv=Hkv, G=G, P=P, ctx=ctx, q_dtype=q_dtype,
+                      scale_lo=100 if wide else 122, scale_hi=150 if wide else 127)
+        got, ref, mag, qkm = run_case(c, max_context=mc)
+        compare(got, ref, mag, qkm, f"attn sweep{n}")
+        live = np.minimum(c["ctx"], mc if mc is not None else c["ctx"].max()) > 0
+        assert np.all(got[~live] == 0.0)                 # rows with no live token give zeros
+
+
 def test_attn_wide_scales_and_single_token_rows():
     # e8m0 bytes 100..150: one live token returns its V (bf16-exact), wide scales elsewhere
     c = make_case(7, R=4, Hkv=1, G=8, P=128, ctx=[1, 1, 260, 1000], scale_lo=100, scale_hi=150)
