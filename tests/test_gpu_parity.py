@@ -333,6 +333,26 @@ def test_explicit_plans_give_identical_outputs():
         assert torch.equal(base_bs.view(torch.int32), obs.view(torch.int32)), pun
 
 
+def test_larger_max_query_len_changes_nothing():
+    # max_query_len only bounds the rows per request: a larger one plans more
+    # (empty) slot blocks, and the outputs stay the same bits
+    wl = W.Workload("mql", "prefill", H=24, page_size=64, q_lens=[19, 0, 41], prefix_lens=[300, 7, 60],
+                    seq_lens=[319, 7, 101], want_logits=True)
+    host = W.make_inputs(wl, 14, "cpu")
+    d = gpu_inputs(host)
+    outs = []
+    for mql in (41, 42, 300):
+        bs, lg = mx.score_prefill(d.q, d.k_data, d.k_scale, d.block_tables[0], d.cu_seqlens_q, d.seq_lens,
+                                  d.prefix_lens, mql, wl.window, S, logits=True)
+        lg2 = mx.score_logits(d.q, d.k_data, d.k_scale, d.block_tables[0], d.cu_seqlens_q, d.seq_lens,
+                              d.prefix_lens, mql, wl.window, S)
+        torch.cuda.synchronize()
+        outs.append((bs.view(torch.int32).clone(), lg.view(torch.int32).clone(), lg2.view(torch.int32).clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(outs[0], o))
+    assert torch.equal(outs[0][1], outs[0][2])
+
+
 def test_graph_replay_with_poisoned_outputs():
     # Captured decode and prefill calls are replayed with outputs poisoned
     # (NaN) in between; every replay must rewrite every element (aiter #5518,
