@@ -83,6 +83,8 @@ def test_row_limits():
     assert topk.row_limits("prefill", [4], 10, [0, 2], [2]).tolist() == [3, 4]
     assert topk.row_limits("prefill", [4, 9], 8, [0, 2, 3], [2, 8]).tolist() == [3, 4, 8]
     assert topk.row_limits("decode", [0, 5, 99], 64).tolist() == [0, 5, 64]
+    # prefix_len + i + 1 past 2^31 - 1: the limit is still seq_len (integers, no wrap)
+    assert topk.row_limits("prefill", [450, 12], 512, [0, 3, 5], [2**31 - 2, 10]).tolist() == [450, 450, 450, 11, 12]
 
 
 def _mutant(kind):
