@@ -127,7 +127,9 @@ typedef struct mxs_query {
 
 /* fp32 output [rows, heads, width], last axis contiguous:
  * element (r, h, x) at ptr + r * row_stride + h * head_stride + x (elements).
- * ptr 4-byte aligned; strides >= 0. A NULL ptr means "not requested". */
+ * ptr 4-byte aligned; strides >= 0. A NULL ptr means "not requested". With
+ * no rows or max_seq_len = 0 a scoring call writes nothing and is a no-op,
+ * and a required output may then be NULL too (an empty tensor's pointer). */
 typedef struct mxs_out {
   float* ptr;
   int64_t row_stride;

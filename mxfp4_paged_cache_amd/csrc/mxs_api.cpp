@@ -664,16 +664,15 @@ int score(int mode, const mxs_query* q, const mxs_kcache* k, const mxs_batch* bt
     return fail(MXS_EINVAL, "total_rows and max_query_len must be >= 0");
   const bool want_bs = bs && bs->ptr;
   const bool want_lg = lg && lg->ptr;
-  if (mode != MXS_MODE_LOGITS && !want_bs) return fail(MXS_EINVAL, "block_scores output is required");
-  if (mode == MXS_MODE_LOGITS && !want_lg) return fail(MXS_EINVAL, "logits output is required in logits mode");
 
   const int32_t H = q->num_heads, P = k->page_size;
   const int64_t rows = decode ? bt->batch : bt->total_rows;
   const int64_t NB = ceil_div(bt->max_seq_len, P);
-  if (rows == 0 || bt->max_seq_len == 0 || bt->batch == 0) {
-    // nothing to write; still refuse descriptors that are wrong regardless of size
-    return MXS_OK;
-  }
+  // Nothing to write: no rows or an empty window. The outputs then hold no
+  // element and may be NULL (an empty tensor's data pointer).
+  if (rows == 0 || bt->max_seq_len == 0 || bt->batch == 0) return MXS_OK;
+  if (mode != MXS_MODE_LOGITS && !want_bs) return fail(MXS_EINVAL, "block_scores output is required");
+  if (mode == MXS_MODE_LOGITS && !want_lg) return fail(MXS_EINVAL, "logits output is required in logits mode");
   // query
   const int64_t es = q->dtype == MXS_Q_BF16 ? 2 : 1;
   if (!q->ptr) return fail(MXS_EINVAL, "query pointer is NULL");

@@ -147,7 +147,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
     need = sum(npr)
     width = max(max(npr, default=0), wl.NB, wl.table_width) + wl.table_pad
     per_table = need if wl.table_fill == "pad" else wl.B * width
-    pool = max(wl.pool_pages, per_table * wl.tables)
+    pool = max(1, wl.pool_pages, per_table * wl.tables)   # the scorers take pools of one page or more
     if wl.layout == "shared":
         pool = max(pool, wl.shared_first_page + need * wl.tables)
 

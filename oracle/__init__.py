@@ -190,7 +190,7 @@ def score(*, mode: str, q: np.ndarray, q_dtype: str, k_data: np.ndarray, k_scale
         qd = MXO_Q_E4M3
     else:
         raise ValueError(q_dtype)
-    assert q.ndim == 3 and q.shape[2] == 128 and q.strides[2] == q.itemsize
+    assert q.ndim == 3 and q.shape[2] == 128 and (q.size == 0 or q.strides[2] == q.itemsize)
     H = q.shape[1]
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)

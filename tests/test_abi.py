@@ -109,6 +109,22 @@ def test_rejects_bad_sm_scale(L, sm):
     assert call(L, q, k, b, bs, lg, sm=sm) == mx.MXS_EINVAL
 
 
+def test_empty_problems_accept_null_outputs(L):
+    # no rows (an empty tensor's data pointer is NULL) or an empty window:
+    # nothing to write, so the required output may be NULL; with rows it may not
+    for field, decode_empty in (("total_rows", False), ("max_seq_len", True), ("batch", True)):
+        q, k, b, bs, lg = valid_args()
+        setattr(b, field, 0)
+        bs.ptr = None
+        assert call(L, q, k, b, bs, lg) == mx.MXS_OK, (field, L.mxs_last_error())
+        # decode rows are the requests: total_rows = 0 leaves one row to score
+        want = mx.MXS_OK if decode_empty else mx.MXS_EINVAL
+        assert call(L, q, k, b, bs, lg, fn="mxs_score_decode") == want, (field, L.mxs_last_error())
+    q, k, b, bs, lg = valid_args()
+    bs.ptr = None
+    assert call(L, q, k, b, bs, lg) == mx.MXS_EINVAL
+
+
 def test_logits_mode_needs_logits(L):
     q, k, b, bs, lg = valid_args()
     assert call(L, q, k, b, lg, bs, fn="mxs_score_logits") == mx.MXS_EINVAL
