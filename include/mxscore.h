@@ -256,9 +256,10 @@ int mxs_write_pages(const void* k, int64_t k_row_stride, int64_t num_tokens, con
  *   are live. NB = ceil(max_seq_len / page_size), at most 4096.
  * mode: MXS_MODE_DECODE (rows are requests; batch->seq_lens used) or
  * MXS_MODE_PREFILL / MXS_MODE_LOGITS (rows per cu_seqlens_q; seq_lens and
- * prefix_lens used). batch->block_table is not read and may be NULL.
- * Strides in elements. Same device contract and asynchrony as the scoring
- * calls; k = 0 or no rows is a no-op. Returns MXS_OK, MXS_EINVAL,
+ * prefix_lens used). batch->block_table is not read and may be NULL; with
+ * max_seq_len = 0 no score is read and block_scores may be NULL (every row
+ * gets k times -1). Strides in elements. Same device contract and asynchrony
+ * as the scoring calls; k = 0 or no rows is a no-op. Returns MXS_OK, MXS_EINVAL,
  * MXS_ELAYOUT, MXS_EUNSUPPORTED (NB > 4096 or not gfx950) or MXS_EDEVICE. */
 int mxs_select_pages(int32_t mode, const mxs_batch* batch, int32_t num_heads, int32_t page_size,
                      const float* block_scores, int64_t bs_row_stride, int64_t bs_head_stride, int32_t k,

@@ -365,7 +365,8 @@ def select_pages(block_scores: torch.Tensor, k: int, seq_lens, max_seq_len: int,
     padded -> int32 [rows, H, k]. Decode rows (one per request) when
     cu_seqlens_q is None, else prefill rows."""
     dev = _same_device(block_scores, seq_lens, cu_seqlens_q, prefix_lens, out)
-    if block_scores.dtype != torch.float32 or block_scores.dim() != 3 or block_scores.stride(2) != 1:
+    if block_scores.dtype != torch.float32 or block_scores.dim() != 3 or (
+            block_scores.numel() > 0 and block_scores.stride(2) != 1):
         raise ValueError("block_scores must be float32 [rows, H, NB] with unit page stride")
     R, H, NB = block_scores.shape
     if NB * page_size < max_seq_len:

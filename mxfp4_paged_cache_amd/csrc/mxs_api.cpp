@@ -194,7 +194,8 @@ int mxs_select_pages(int32_t mode, const mxs_batch* bt, int32_t num_heads, int32
   if (NB > mxs::kSelectMaxPages)
     return fail(MXS_EUNSUPPORTED, "selection holds at most %d pages per row, got %lld", mxs::kSelectMaxPages,
                 (long long)NB);
-  if (!block_scores || !pages) return fail(MXS_EINVAL, "block_scores and pages must not be NULL");
+  // an empty window (NB = 0) reads no score, and its score tensor may be empty (NULL)
+  if ((!block_scores && NB > 0) || !pages) return fail(MXS_EINVAL, "block_scores and pages must not be NULL");
   if (!aligned(block_scores, 4) || !aligned(pages, 4)) return fail(MXS_ELAYOUT, "buffers must be 4-byte aligned");
   if (!bt->seq_lens || (!decode && (!bt->cu_seqlens_q || !bt->prefix_lens)))
     return fail(MXS_EINVAL, "seq_lens (and for prefill cu_seqlens_q, prefix_lens) must not be NULL");

@@ -286,6 +286,14 @@ def test_select_pages_rejections_before_device_work(L):
     assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4, rs=64 * 4097, hs=4097) == mx.MXS_EUNSUPPORTED
     wide.max_seq_len = 2**31 - 255
     assert sel(mx.MXS_MODE_PREFILL, wide, 64, 128, 4) == mx.MXS_EINVAL
+    # an empty window reads no score: a NULL score tensor is taken (up to the device check)
+    empty = mx.Batch.from_buffer_copy(bytes(b))
+    empty.max_seq_len = 0
+    rc = L.mxs_select_pages(mx.MXS_MODE_PREFILL, ctypes.byref(empty), 64, 128, None, 0, 0, 4, FAKE + 0x10000, 64 * 4,
+                            4, None)
+    assert rc != mx.MXS_EINVAL or b"NULL" not in L.mxs_last_error(), L.mxs_last_error()
+    assert L.mxs_select_pages(mx.MXS_MODE_PREFILL, ctypes.byref(b), 64, 128, None, 64 * 8, 8, 4, FAKE + 0x10000,
+                              64 * 4, 4, None) == mx.MXS_EINVAL                          # scores needed when NB > 0
 
 
 def test_write_pages_rejections_before_device_work(L):

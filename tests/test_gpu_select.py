@@ -273,5 +273,10 @@ def test_empty_window_reads_nothing_and_pads():
     cu = torch.tensor([0, 2, 5], dtype=torch.int32, device="cuda")
     got_p = mx.select_pages(bs, k, torch.zeros(2, dtype=torch.int32, device="cuda"), 0, 128, cu_seqlens_q=cu,
                             prefix_lens=torch.zeros(2, dtype=torch.int32, device="cuda"))
+    # the same with an empty score tensor (NULL data pointer), and a call with no rows
+    got_e = mx.select_pages(torch.empty((R, H, 0), device="cuda"), k, seq, 0, 64)
+    none = mx.select_pages(torch.empty((0, H, 7), device="cuda"), k, torch.zeros(0, dtype=torch.int32, device="cuda"),
+                           7 * 64, 64)
     torch.cuda.synchronize()
-    assert (got == -1).all() and (got_p == -1).all()
+    assert (got == -1).all() and (got_p == -1).all() and (got_e == -1).all()
+    assert none.shape == (0, H, k)
