@@ -149,7 +149,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", q_strided: bool = Fal
     per_table = need if wl.table_fill == "pad" else wl.B * width
     pool = max(1, wl.pool_pages, per_table * wl.tables)   # the scorers take pools of one page or more
     if wl.layout == "shared":
-        pool = max(pool, wl.shared_first_page + need * wl.tables)
+        pool = max(pool, wl.shared_first_page + per_table * wl.tables)
 
     gd = _gen(seed, F_KDATA, device)
     gs = _gen(seed, F_KSCALE, device)

@@ -153,6 +153,8 @@ def compare(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, sm_scale: float, 
 
 def argmax_pages(x: np.ndarray) -> np.ndarray:
     """Argmax over the last axis, lowest index on ties, -1 where every value is -inf."""
+    if x.shape[-1] == 0:                     # an empty window: no page at all
+        return np.full(x.shape[:-1], -1, dtype=np.int64)
     a = np.argmax(x, axis=-1)
     return np.where(np.all(np.isneginf(x), axis=-1), -1, a)
 
