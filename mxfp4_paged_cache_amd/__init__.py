@@ -166,7 +166,7 @@ def _query(q: torch.Tensor) -> Query:
         dt = MXS_Q_E4M3
     else:
         raise ValueError(f"query dtype must be bfloat16 or float8_e4m3fn, got {q.dtype} (fp16 is refused)")
-    if q.stride(2) != 1:
+    if q.numel() > 0 and q.stride(2) != 1:     # an empty tensor's strides carry no layout
         raise ValueError("query head_dim must be contiguous")
     return Query(q.data_ptr(), dt, q.stride(0), q.stride(1), q.shape[1])
 
@@ -213,7 +213,8 @@ def _int_vec(name: str, t: Optional[torch.Tensor], n: int) -> int:
 
 
 def _table(block_table: torch.Tensor) -> Tuple[int, int, int]:
-    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or (
+            block_table.numel() > 0 and block_table.stride(1) != 1):
         raise ValueError("block_table must be an int32 [batch, width] tensor with contiguous rows")
     return block_table.data_ptr(), block_table.stride(0), block_table.shape[1]
 
@@ -398,7 +399,7 @@ def write_pages(k: torch.Tensor, slot_mapping: torch.Tensor, k_data, k_scale, st
     OCP MX conversion; with k_scale None, into an fp8 cache (128 e4m3 bytes
     per token, nearest even, saturating). Writes the cache views in place."""
     dev = _same_device(k, slot_mapping, k_data, k_scale)
-    if k.dtype != torch.bfloat16 or k.dim() != 2 or k.shape[1] != 128 or k.stride(1) != 1:
+    if k.dtype != torch.bfloat16 or k.dim() != 2 or k.shape[1] != 128 or (k.numel() > 0 and k.stride(1) != 1):
         raise ValueError("k must be bf16 [N, 128] with contiguous head_dim")
     if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int64 vector")
@@ -444,7 +445,7 @@ def attn_decode(q: torch.Tensor, k_data, k_scale, v_data, v_scale, block_table: 
         raise ValueError("block_table has fewer rows than the query")
     if out is None:
         out = torch.empty((R, Hq, 128), dtype=torch.bfloat16, device=dev)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (R, Hq, 128) or out.stride(2) != 1:
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (R, Hq, 128) or (out.numel() > 0 and out.stride(2) != 1):
         raise ValueError(f"out must be bf16 [{R}, {Hq}, 128] with a contiguous last axis")
     kv = KVCache(kview, vview, P, Hkv, pages)
     with torch.cuda.device(dev):

@@ -356,6 +356,22 @@ def test_calls_with_nothing_to_write():
     assert bs.shape == (2, 16, 0)
 
 
+def test_empty_tensors_with_zero_strides():
+    # empty tensors made from numpy arrays have all-zero strides: with nothing
+    # to read or write, every call takes them
+    z = lambda shape, dt: torch.from_numpy(np.zeros(shape, dt)).cuda()
+    q0 = z((0, 8, 128), np.int16).view(torch.bfloat16)
+    kd, ks = z((3, 64, 64), np.uint8), z((3, 64, 4), np.uint8)
+    bt0 = z((2, 0), np.int32)
+    cu, seq, pre = (torch.tensor(v, dtype=torch.int32, device="cuda") for v in ([0, 0, 0], [10, 0], [10, 0]))
+    bs, lg = mx.score_prefill(q0, kd, ks, bt0, cu, seq, pre, 0, 0, S, logits=True)
+    assert bs.shape == (0, 8, 0) and lg.shape == (0, 8, 0)
+    sel = mx.select_pages(z((0, 8, 0), np.float32), 4, z((0,), np.int32), 0, 64)
+    assert sel.shape == (0, 8, 4)
+    mx.write_pages(z((0, 128), np.int16).view(torch.bfloat16), z((0,), np.int64), kd, ks)
+    torch.cuda.synchronize()
+
+
 def test_larger_max_query_len_changes_nothing():
     # max_query_len only bounds the rows per request: a larger one plans more
     # (empty) slot blocks, and the outputs stay the same bits
